@@ -1,0 +1,146 @@
+/*
+ * pa.h - paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  Every pointer argument is a DEVICE
+ * pointer owned by the caller unless stated otherwise; the library never
+ * allocates, frees or synchronises on these calls.  Work is enqueued on the
+ * caller's HIP stream (`stream` is a hipStream_t; NULL means the default
+ * stream) and calls on one stream run in order:
+ *     pa_reshape_and_cache -> pa_decode -> pa_decode_reduce.
+ *
+ * What is computed.  A paged KV cache holds keys and values in fixed-size
+ * physical blocks; a per-sequence block table maps logical block j of
+ * sequence b to physical block block_tables[b][j], and token t of the
+ * sequence lives at slot t % block_size of that block (ovshake/nano-vllm
+ * README, "Key Concepts Explained: PagedAttention"; flex-nano-vllm README,
+ * file list: page table and paged kv cache).  In the decode phase each
+ * sequence contributes one new token (same README, "Key Concepts Explained:
+ * KV Cache"), whose query attends to the sequence's cached keys:
+ *     s_t = scale * q . k_t                      (X-Ray Mode, Step 2)
+ *     s_t = softcap * tanh(s_t / softcap)        if softcap > 0
+ *     out = sum_t softmax(s)_t v_t   over t in [max(0, L - window), L)
+ * Query head h reads KV head floor(h / G), G = num_heads / num_kv_heads
+ * (grouped-query attention; X-Ray Mode, Step 1 GQA note).  The soft-cap and
+ * the window follow the public Gemma-2 attention definition (the pages name
+ * Gemma 2 but print neither rule).
+ *
+ * Layouts (row-major, innermost last):
+ *   q, out          [num_seqs, num_heads, head_dim]               dtype
+ *   key, value      [num_tokens, num_kv_heads, head_dim]          dtype
+ *   k_cache,v_cache [num_blocks, block_size, num_kv_heads, head_dim] dtype
+ *   block_tables    [num_seqs, max_blocks_per_seq] int32 physical ids
+ *   context_lens    [num_seqs] int32: tokens in the sequence, counting the
+ *                   new one (whose K/V reshape_and_cache has written)
+ *   slot_mapping    [num_tokens] int64: physical_block*block_size + offset,
+ *                   or -1 to skip the token
+ *
+ * Errors.  Every call returns PA_OK (0) or a negative pa_status.  All checks
+ * on host-visible arguments run before anything is enqueued, so a failed call
+ * leaves every buffer untouched.  Device-resident contents are the caller's
+ * contract and are not checked on the host: block ids referenced by the first
+ * ceil(L/block_size) table entries lie in [0, num_blocks), context_lens[b] <=
+ * max_context_len, and slot_mapping holds no duplicate slot.  The kernels
+ * clamp out-of-range ids and lengths so that a broken contract gives wrong
+ * numbers rather than an out-of-bounds access.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_EINVAL = -1,        /* bad pointer, size or value                      */
+  PA_EUNSUPPORTED = -2,  /* valid but not built: dtype, head_dim, group size */
+  PA_EWORKSPACE = -3,    /* workspace missing or smaller than required      */
+  PA_ELAUNCH = -4        /* the HIP runtime refused the launch              */
+} pa_status;
+
+/* Text for a status code (static storage, never NULL). */
+const char* pa_status_string(int status);
+
+/*
+ * Write the K/V rows of new tokens into their physical slots:
+ *   k_cache.flat[slot_mapping[i]] = key[i], v_cache.flat[...] = value[i]
+ * with flat = view [num_blocks*block_size, num_kv_heads, head_dim].  Rows
+ * with slot -1 are skipped; slots outside the pool are skipped as well.  The
+ * copy is bit-exact (NaN payloads included).  Other slots are not touched.
+ * Supported: dtype any; head_dim in {64,128,256}; block_size a power of two
+ * in [1,256]; num_tokens >= 0 (0 is a no-op).
+ */
+int pa_reshape_and_cache(const void* key, const void* value,
+                         void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int num_tokens,
+                         int num_blocks, int block_size, int num_kv_heads,
+                         int head_dim, pa_dtype dtype, void* stream);
+
+/*
+ * The partition size the library would pick for this shape (tokens per
+ * split-K partition; 0 means one partition per sequence).  Host-only.
+ */
+int pa_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads,
+                             int head_dim, int block_size, int max_context_len,
+                             int window, pa_dtype dtype);
+
+/*
+ * Bytes of workspace pa_decode needs for split-K partials:
+ *   tmp_out    [num_seqs, num_heads, NP, head_dim] float32
+ *   max_logits [num_seqs, num_heads, NP]           float32 (base-2 logits)
+ *   exp_sums   [num_seqs, num_heads, NP]           float32
+ * with NP = ceil(max_context_len / partition_size).  0 when partition_size
+ * is 0 or NP <= 1.  Host-only.
+ */
+size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim,
+                                int max_context_len, int partition_size);
+
+/*
+ * Decode attention, first pass.  The keys of each sequence are split at
+ * absolute positions that are multiples of partition_size (0 = one partition
+ * per sequence).  A sequence whose attended keys fall in a single partition
+ * gets its output written to `out` directly; for the others each partition
+ * writes normalised partial outputs plus its running max and sum to the
+ * workspace, and pa_decode_reduce must follow on the same stream.
+ * An empty sequence (context_lens[b] == 0) gets out = 0.
+ *   scale          multiplies q . k (e.g. 1/sqrt(head_dim))
+ *   softcap        > 0: logits capped to softcap*tanh(s/softcap); 0: off
+ *   window         > 0: attend to the last `window` keys only; 0: off
+ *   max_context_len  host-side upper bound of context_lens (sizes the grid);
+ *                  must be <= max_blocks_per_seq * block_size
+ *   partition_size 0, or a positive multiple of block_size
+ * Supported: num_heads/num_kv_heads in {1,2,4,8}; head_dim in {64,128,256};
+ * block_size a power of two in [1,256]; dtype f32, f16, bf16 (q, caches and
+ * out share it; arithmetic is float32).
+ */
+int pa_decode(void* out, void* workspace, size_t workspace_bytes,
+              const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, int max_blocks_per_seq,
+              const int32_t* context_lens, int max_context_len,
+              int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+              int block_size, int num_blocks, float scale, float softcap,
+              int window, int partition_size, pa_dtype dtype, void* stream);
+
+/*
+ * Decode attention, reduce pass: for each sequence with more than one
+ * non-empty partition, combine the partials with weights
+ * exp_sum_p * 2^(max_logit_p - max_p' max_logit_p') and write `out`.
+ * Sequences handled by pa_decode alone are left as they are.  A no-op when
+ * partition_size is 0.  Arguments must match the pa_decode call.
+ */
+int pa_decode_reduce(void* out, const void* workspace, size_t workspace_bytes,
+                     const int32_t* context_lens, int max_context_len,
+                     int num_seqs, int num_heads, int head_dim,
+                     int partition_size, int window, pa_dtype dtype,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,13 @@
+"""Paged KV-cache decode attention for AMD MI355X (gfx950).
+
+Hand-written HIP kernels behind a C ABI (include/pa.h, libpa.so); this
+package is a thin binding that marshals torch tensors (device memory) and
+torch's current stream into those calls.
+"""
+from ._lib import EXPORTS, LIB_PATH, PaError, load, status_string
+from .ops import (alloc_workspace, decode, decode_partitions, decode_reduce,
+                  partition_size, reshape_and_cache, workspace_size)
+
+__all__ = ["EXPORTS", "LIB_PATH", "PaError", "load", "status_string", "alloc_workspace",
+           "decode", "decode_partitions", "decode_reduce", "partition_size",
+           "reshape_and_cache", "workspace_size"]

@@ -1,0 +1,65 @@
+"""ctypes loader for libpa.so and the raw C entry points.
+
+The library must be built in-tree first (``python -m
+paged_kv_decode_pa_amd.build``); loading fails loudly when it is missing.
+There is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpa.so")
+
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+STATUS = {0: "PA_OK", -1: "PA_EINVAL", -2: "PA_EUNSUPPORTED", -3: "PA_EWORKSPACE",
+          -4: "PA_ELAUNCH"}
+
+# every symbol include/pa.h declares
+EXPORTS = ("pa_status_string", "pa_reshape_and_cache", "pa_decode_partition_size",
+           "pa_decode_workspace_size", "pa_decode", "pa_decode_reduce")
+
+_lib = None
+
+
+class PaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m paged_kv_decode_pa_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64p, sz, f32 = (ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                             ctypes.c_size_t, ctypes.c_float)
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_status_string.argtypes = [i32]
+    lib.pa_reshape_and_cache.restype = i32
+    lib.pa_reshape_and_cache.argtypes = [vp, vp, vp, vp, i64p, i32, i32, i32, i32, i32, i32, vp]
+    lib.pa_decode_partition_size.restype = i32
+    lib.pa_decode_partition_size.argtypes = [i32] * 8
+    lib.pa_decode_workspace_size.restype = sz
+    lib.pa_decode_workspace_size.argtypes = [i32] * 5
+    lib.pa_decode.restype = i32
+    lib.pa_decode.argtypes = [vp, vp, sz, vp, vp, vp, vp, i32, vp, i32,
+                              i32, i32, i32, i32, i32, i32, f32, f32, i32, i32, i32, vp]
+    lib.pa_decode_reduce.restype = i32
+    lib.pa_decode_reduce.argtypes = [vp, vp, sz, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().pa_status_string(status).decode()
+
+
+def check(fn: str, status: int) -> None:
+    if status != 0:
+        raise PaError(fn, status)

@@ -1,0 +1,76 @@
+"""Build libpa.so (gfx950) in-tree with hipcc.
+
+    python -m paged_kv_decode_pa_amd.build        # or build() from Python
+
+Every HIP source under csrc/ is compiled in parallel, then linked into
+paged_kv_decode_pa_amd/libpa.so.  Packed-FP32 instruction selection is
+switched off for device code (see the packed-fp32-ops flag below).
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import glob
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libpa.so")
+ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
+
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-I", os.path.join(ROOT, "include"),
+    # device code: no packed FP32 arithmetic (v_pk_*_f32)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def _compile(src: str, obj: str, verbose: bool):
+    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    # hipcc's host pass does not know the device-only feature flag
+    text = "\n".join(l for l in r.stdout.decode(errors="replace").splitlines()
+                     if "packed-fp32-ops" not in l)
+    return src, r.returncode, text
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    srcs = sources()
+    tmp = tempfile.mkdtemp(prefix="pa_build_")
+    try:
+        objs = [os.path.join(tmp, os.path.basename(s) + ".o") for s in srcs]
+        with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+            results = list(ex.map(lambda a: _compile(a[0], a[1], verbose), zip(srcs, objs)))
+        failed = [(s, t) for s, rc, t in results if rc != 0]
+        if verbose:
+            for s, rc, t in results:
+                if rc == 0 and t.strip():
+                    print(t)
+        if failed:
+            for src, text in failed:
+                print(f"--- {src}\n{text}", file=sys.stderr)
+            raise RuntimeError("hipcc failed for " + ", ".join(os.path.basename(s) for s, _ in failed))
+        tmp_lib = LIB + ".tmp"
+        cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp_lib, *objs]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp_lib, LIB)
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

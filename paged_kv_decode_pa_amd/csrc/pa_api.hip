@@ -1,0 +1,241 @@
+// C ABI of the library: argument checks, shape-dependent choices and kernel
+// launches on the caller's stream.  Nothing here allocates, frees or
+// synchronises.
+#include <math.h>
+#include <stdlib.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/pa.h"
+#include "pa_launch.h"
+#include "pa_reshape.h"
+
+namespace {
+
+// MI355X: 256 compute units.  Used only to size work, never for correctness.
+constexpr int kNumCUs = 256;
+
+bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+int ilog2(int v) {
+  int r = 0;
+  while ((1 << r) < v) ++r;
+  return r;
+}
+
+bool supported_head_dim(int d) { return d == 64 || d == 128 || d == 256; }
+bool valid_dtype(int dt) { return dt == PA_F32 || dt == PA_F16 || dt == PA_BF16; }
+int elem_bytes(int dt) { return dt == PA_F32 ? 4 : 2; }
+
+int num_parts(int max_context_len, int partition_size) {
+  if (partition_size <= 0 || max_context_len <= 0) return 1;
+  return (max_context_len + partition_size - 1) / partition_size;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  if (!v || !*v) return dflt;
+  return atoi(v);
+}
+
+// Wavefronts per workgroup: enough to split a partition's chunks while each
+// wavefront still streams several of them.  PA_DECODE_WAVES overrides.
+int waves_for(int tokens_per_part, int chunk_tokens, int units) {
+  int forced = env_int("PA_DECODE_WAVES", 0);
+  if (forced >= 1 && forced <= pa::kMaxWaves) return forced;
+  int chunks = (tokens_per_part + chunk_tokens - 1) / chunk_tokens;
+  int nw = 1;
+  while (nw < pa::kMaxWaves && chunks >= 4 * nw * 2 && units * nw < 8 * 4 * kNumCUs) nw *= 2;
+  return nw;
+}
+
+int chunk_tokens(int dt, int D, int G) {
+  const int epl = 16 / elem_bytes(dt);
+  const int lpr = D / epl;
+  const int rpi = 64 / lpr;
+  const int ni = G >= 8 ? 4 : 8;
+  return rpi * ni;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_EINVAL: return "invalid argument";
+    case PA_EUNSUPPORTED: return "unsupported shape or dtype";
+    case PA_EWORKSPACE: return "workspace missing or too small";
+    case PA_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int num_tokens, int num_blocks,
+                         int block_size, int num_kv_heads, int head_dim, pa_dtype dtype,
+                         void* stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PA_EINVAL;
+  if (!valid_dtype(dtype) || !supported_head_dim(head_dim) || !pow2_in(block_size, 1, 256))
+    return PA_EUNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_EINVAL;
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * elem_bytes(dtype);
+  const int row16 = (int)(row_bytes / 16);
+  const int64_t num_slots = (int64_t)num_blocks * block_size;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  pa::reshape_cache_kernel<<<dim3(num_tokens), dim3(256), 0, s>>>(
+      static_cast<const uint4*>(key), static_cast<const uint4*>(value),
+      static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), slot_mapping, num_slots, row16);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
+int pa_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                             int block_size, int max_context_len, int window, pa_dtype dtype) {
+  (void)num_heads;
+  (void)head_dim;
+  (void)dtype;
+  if (num_seqs <= 0 || num_kv_heads <= 0 || block_size <= 0 || max_context_len <= 0) return 0;
+  int forced = env_int("PA_DECODE_PARTITION", -1);
+  if (forced >= 0) return forced;
+  const int span = window > 0 ? (window < max_context_len ? window : max_context_len)
+                              : max_context_len;
+  const long units = (long)num_seqs * num_kv_heads;
+  // plenty of (sequence, head) units and short contexts: no split
+  if (units >= 4L * kNumCUs && span <= 2048) return 0;
+  int part = 512;
+  if (part % block_size) part = block_size;
+  return part;
+}
+
+size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim, int max_context_len,
+                                int partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || partition_size <= 0) return 0;
+  const int np = num_parts(max_context_len, partition_size);
+  if (np <= 1) return 0;
+  const size_t rows = (size_t)num_seqs * num_heads * np;
+  return rows * head_dim * sizeof(float) + 2 * rows * sizeof(float);
+}
+
+int pa_decode(void* out, void* workspace, size_t workspace_bytes, const void* q,
+              const void* k_cache, const void* v_cache, const int32_t* block_tables,
+              int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+              int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+              int num_blocks, float scale, float softcap, int window, int partition_size,
+              pa_dtype dtype, void* stream) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || max_context_len < 0 || window < 0 || partition_size < 0)
+    return PA_EINVAL;
+  if (num_heads % num_kv_heads) return PA_EINVAL;
+  if (!isfinite(scale) || !(softcap >= 0.0f) || !isfinite(softcap)) return PA_EINVAL;
+  if (!valid_dtype(dtype) || !supported_head_dim(head_dim) || !pow2_in(block_size, 1, 256))
+    return PA_EUNSUPPORTED;
+  const int G = num_heads / num_kv_heads;
+  if (!(G == 1 || G == 2 || G == 4 || G == 8)) return PA_EUNSUPPORTED;
+  if (partition_size > 0 && partition_size % block_size) return PA_EINVAL;
+  if ((long)max_context_len > (long)max_blocks_per_seq * block_size) return PA_EINVAL;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_EINVAL;
+
+  const int np = num_parts(max_context_len, partition_size);
+  const size_t need = pa_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
+                                               partition_size);
+  if (need && (!workspace || workspace_bytes < need)) return PA_EWORKSPACE;
+
+  pa::DecodeParams p{};
+  p.out = out;
+  if (need) {
+    const size_t rows = (size_t)num_seqs * num_heads * np;
+    float* ws = static_cast<float*>(workspace);
+    p.tmp_out = ws;
+    p.max_logits = ws + rows * head_dim;
+    p.exp_sums = p.max_logits + rows;
+  }
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.max_context_len = max_context_len;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.num_blocks = num_blocks;
+  p.log2_bs = ilog2(block_size);
+  p.window = window;
+  p.part = partition_size > 0 ? partition_size : (max_context_len > 0 ? max_context_len : 1);
+  p.num_parts = np;
+  if (softcap > 0.0f) {
+    p.qk_mul = scale / softcap;
+    p.cap_mul = softcap * pa::kLog2e;
+  } else {
+    p.qk_mul = scale * pa::kLog2e;
+    p.cap_mul = 0.0f;
+  }
+
+  const int nt = chunk_tokens(dtype, head_dim, G);
+  const int span = window > 0 && window < p.part ? window : p.part;
+  const long units = (long)num_seqs * num_kv_heads * np;
+  const int nw = waves_for(span, nt, (int)(units < (1L << 30) ? units : (1L << 30)));
+  const long blocks = (long)num_seqs * num_kv_heads * np;
+  if (blocks > 0x7fffffffL) return PA_EUNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)blocks), block(64 * nw);
+  bool ok = false;
+  switch (dtype) {
+    case PA_F32: ok = pa::launch_decode_f32(head_dim, G, grid, block, s, p); break;
+    case PA_F16: ok = pa::launch_decode_f16(head_dim, G, grid, block, s, p); break;
+    case PA_BF16: ok = pa::launch_decode_bf16(head_dim, G, grid, block, s, p); break;
+  }
+  if (!ok) return PA_EUNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
+int pa_decode_reduce(void* out, const void* workspace, size_t workspace_bytes,
+                     const int32_t* context_lens, int max_context_len, int num_seqs,
+                     int num_heads, int head_dim, int partition_size, int window,
+                     pa_dtype dtype, void* stream) {
+  if (num_seqs < 0 || num_heads <= 0 || max_context_len < 0 || window < 0 || partition_size < 0)
+    return PA_EINVAL;
+  if (!valid_dtype(dtype) || !supported_head_dim(head_dim)) return PA_EUNSUPPORTED;
+  const size_t need = pa_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
+                                               partition_size);
+  if (num_seqs == 0 || need == 0) return PA_OK;
+  if (!out || !context_lens) return PA_EINVAL;
+  if (!workspace || workspace_bytes < need) return PA_EWORKSPACE;
+  const int np = num_parts(max_context_len, partition_size);
+  const size_t rows = (size_t)num_seqs * num_heads * np;
+  const float* ws = static_cast<const float*>(workspace);
+  pa::ReduceParams p{};
+  p.out = out;
+  p.tmp_out = ws;
+  p.max_logits = ws + rows * head_dim;
+  p.exp_sums = p.max_logits + rows;
+  p.context_lens = context_lens;
+  p.max_context_len = max_context_len;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.window = window;
+  p.part = partition_size;
+  p.num_parts = np;
+  const long waves = (long)num_seqs * num_heads;
+  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+#define PA_REDUCE_CASE(DTV, DT)                                                   \
+  case DTV:                                                                       \
+    if (head_dim == 64) pa::reduce_kernel<DT, 64><<<grid, block, 0, s>>>(p);      \
+    else if (head_dim == 128) pa::reduce_kernel<DT, 128><<<grid, block, 0, s>>>(p); \
+    else pa::reduce_kernel<DT, 256><<<grid, block, 0, s>>>(p);                   \
+    break;
+  switch (dtype) {
+    PA_REDUCE_CASE(PA_F32, pa::DT_F32)
+    PA_REDUCE_CASE(PA_F16, pa::DT_F16)
+    PA_REDUCE_CASE(PA_BF16, pa::DT_BF16)
+  }
+#undef PA_REDUCE_CASE
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
+}  // extern "C"

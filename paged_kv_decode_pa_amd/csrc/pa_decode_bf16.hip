@@ -1,0 +1,6 @@
+// Decode-kernel instantiations for bf16 storage.
+#include "pa_launch.h"
+
+namespace pa {
+PA_DEFINE_DECODE_LAUNCHER(launch_decode_bf16, DT_BF16)
+}  // namespace pa

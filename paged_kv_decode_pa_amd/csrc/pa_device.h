@@ -1,0 +1,197 @@
+// Device-side building blocks shared by the gfx950 kernels: storage types,
+// 16-byte row fragments, wavefront reductions and number conversions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+template <int DT> struct Elem;
+template <> struct Elem<DT_F32>  { static constexpr int bytes = 4; };
+template <> struct Elem<DT_F16>  { static constexpr int bytes = 2; };
+template <> struct Elem<DT_BF16> { static constexpr int bytes = 2; };
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// 16-byte fragments: one lane's share of a K/V/q row
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// Streaming load of K/V data: every byte is read once per decode step, so
+// mark it non-temporal to keep it from displacing reusable lines.
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+  uint4 r;
+  r.x = __builtin_nontemporal_load(&q->x);
+  r.y = __builtin_nontemporal_load(&q->y);
+  r.z = __builtin_nontemporal_load(&q->z);
+  r.w = __builtin_nontemporal_load(&q->w);
+  return r;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// Dot product of a 16-byte K fragment with the matching q fragment, added
+// to acc.  16-bit types use the packed two-way dot instructions (products of
+// two 16-bit floats are exact in float32).
+template <int DT>
+__device__ __forceinline__ float dot16(const uint4& k, const uint4& q, float acc);
+
+template <>
+__device__ __forceinline__ float dot16<DT_BF16>(const uint4& k, const uint4& q, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.x),
+                                        __builtin_bit_cast(bf16x2_t, q.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.y),
+                                        __builtin_bit_cast(bf16x2_t, q.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.z),
+                                        __builtin_bit_cast(bf16x2_t, q.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, k.w),
+                                        __builtin_bit_cast(bf16x2_t, q.w), acc, false);
+  return acc;
+}
+
+template <>
+__device__ __forceinline__ float dot16<DT_F16>(const uint4& k, const uint4& q, float acc) {
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, k.x),
+                               __builtin_bit_cast(f16x2_t, q.x), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, k.y),
+                               __builtin_bit_cast(f16x2_t, q.y), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, k.z),
+                               __builtin_bit_cast(f16x2_t, q.z), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, k.w),
+                               __builtin_bit_cast(f16x2_t, q.w), acc, false);
+  return acc;
+}
+
+template <>
+__device__ __forceinline__ float dot16<DT_F32>(const uint4& k, const uint4& q, float acc) {
+  acc = fmaf(__uint_as_float(k.x), __uint_as_float(q.x), acc);
+  acc = fmaf(__uint_as_float(k.y), __uint_as_float(q.y), acc);
+  acc = fmaf(__uint_as_float(k.z), __uint_as_float(q.z), acc);
+  acc = fmaf(__uint_as_float(k.w), __uint_as_float(q.w), acc);
+  return acc;
+}
+
+// Widen a 16-byte fragment to float32 (exact for every storage type).
+template <int DT>
+__device__ __forceinline__ void widen16(const uint4& v, float* o);
+
+template <>
+__device__ __forceinline__ void widen16<DT_BF16>(const uint4& v, float* o) {
+  o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+  o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
+}
+template <>
+__device__ __forceinline__ void widen16<DT_F16>(const uint4& v, float* o) {
+  o[0] = f16_lo(v.x); o[1] = f16_hi(v.x); o[2] = f16_lo(v.y); o[3] = f16_hi(v.y);
+  o[4] = f16_lo(v.z); o[5] = f16_hi(v.z); o[6] = f16_lo(v.w); o[7] = f16_hi(v.w);
+}
+template <>
+__device__ __forceinline__ void widen16<DT_F32>(const uint4& v, float* o) {
+  o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+  o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
+}
+
+// ---------------------------------------------------------------------------
+// float32 -> storage type, round to nearest even
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)(0x7fc0u | ((u >> 16) & 0x8000u));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+template <int DT>
+__device__ __forceinline__ void store_elem(void* base, size_t idx, float x) {
+  if constexpr (DT == DT_F32) {
+    reinterpret_cast<float*>(base)[idx] = x;
+  } else if constexpr (DT == DT_F16) {
+    reinterpret_cast<uint16_t*>(base)[idx] = f32_to_f16_bits(x);
+  } else {
+    reinterpret_cast<uint16_t*>(base)[idx] = f32_to_bf16_bits(x);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// math
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// tanh from its definition: tanh|x| = 1 - 2 / (e^{2|x|} + 1), sign restored.
+// Absolute error is a few float32 ulps of 1.
+__device__ __forceinline__ float tanh_def(float x) {
+  float ax = fabsf(x);
+  float e = fast_exp2(ax * (2.0f * kLog2e));
+  float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+  return copysignf(t, x);
+}
+
+// ---------------------------------------------------------------------------
+// wavefront reductions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// Reduce-scatter of N independent partial sums across the LPR lanes of an
+// aligned lane group.  Step by step (masks LPR/2 .. 1) each lane keeps half
+// of its values and adds the partner's copy of that half, so every shuffle
+// moves useful data.  Afterwards lane holds max(1, N/LPR) complete sums in
+// v[0..): those with indices tr_base(lane) + t.  When N < LPR the last steps
+// are plain butterflies and neighbouring lanes hold the same sum.
+template <int CUR, int M, int N>
+struct TransposeReduce {
+  static __device__ __forceinline__ void run(float (&v)[N], int lane) {
+    if constexpr (M >= 1) {
+      if constexpr (CUR > 1) {
+        constexpr int H = CUR / 2;
+        const bool up = (lane & M) != 0;
+#pragma unroll
+        for (int j = 0; j < H; ++j) {
+          float send = up ? v[j] : v[j + H];
+          float keep = up ? v[j + H] : v[j];
+          v[j] = keep + shfl_xor_f(send, M);
+        }
+        TransposeReduce<H, M / 2, N>::run(v, lane);
+      } else {
+        v[0] += shfl_xor_f(v[0], M);
+        TransposeReduce<1, M / 2, N>::run(v, lane);
+      }
+    }
+  }
+};
+
+template <int N, int LPR>
+__device__ __forceinline__ int tr_base(int lane) {
+  int base = 0;
+  int cur = N;
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) {
+    if (cur > 1) {
+      cur >>= 1;
+      if (lane & m) base += cur;
+    }
+  }
+  return base;
+}
+
+}  // namespace pa

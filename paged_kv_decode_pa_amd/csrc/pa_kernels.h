@@ -1,0 +1,375 @@
+// gfx950 kernels for paged decode attention: the split-K decode pass, the
+// partition reduce and the KV-cache scatter.
+//
+// Decode work unit: one workgroup per (sequence b, KV head g, partition p),
+// with 1..4 wavefronts that take the partition's chunks round-robin and are
+// merged in LDS at the end.  Within a wavefront:
+//   * a K/V row of head g (D elements) is spread over LPR lanes, 16 bytes
+//     per lane, so one load instruction fetches RPI = 64/LPR whole rows and a
+//     chunk of NI instructions covers NT = RPI*NI tokens with coalesced 16-B
+//     loads (a whole page when block_size == NT);
+//   * the G query heads that share KV head g stay in registers as 16-byte
+//     fragments matching the lane's slice of every row;
+//   * q.k partial sums (NI rows x G heads per lane) are reduce-scattered
+//     across the LPR lanes of a row, one useful value per shuffle;
+//   * the chunk's logits go through LDS, where lane l owns query head l % G
+//     for the online-softmax update (max and sum by xor shuffles), and the
+//     resulting probabilities are read back as broadcasts for P.V;
+//   * P.V accumulates into G x (elements per lane) float32 registers.
+// Next-chunk K loads are issued as soon as the current K fragments are
+// consumed and next-chunk V loads as soon as P.V is done, so each wavefront
+// keeps a chunk of K and V in flight while it computes.
+#pragma once
+
+#include "pa_device.h"
+
+namespace pa {
+
+constexpr int kMaxWaves = 4;
+
+struct DecodeParams {
+  void* out;               // [B, Hq, D]
+  float* tmp_out;          // [B, Hq, NP, D]
+  float* max_logits;       // [B, Hq, NP], base-2 logits
+  float* exp_sums;         // [B, Hq, NP]
+  const void* q;           // [B, Hq, D]
+  const void* k_cache;     // [NB, bs, Hkv, D]
+  const void* v_cache;
+  const int32_t* block_tables;  // [B, max_blocks_per_seq]
+  const int32_t* context_lens;  // [B]
+  int max_blocks_per_seq;
+  int max_context_len;
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int num_blocks;
+  int log2_bs;
+  int window;              // > 0: last `window` keys only
+  int part;                // partition size in tokens (> 0)
+  int num_parts;           // NP
+  float qk_mul;            // multiplies q.k
+  float cap_mul;           // > 0: logit2 = cap_mul * tanh(q.k * qk_mul)
+};
+
+struct ReduceParams {
+  void* out;
+  const float* tmp_out;
+  const float* max_logits;
+  const float* exp_sums;
+  const int32_t* context_lens;
+  int max_context_len;
+  int num_seqs;
+  int num_heads;
+  int window;
+  int part;
+  int num_parts;
+};
+
+template <int DT, int D, int G>
+struct DecodeShape {
+  static constexpr int EB = Elem<DT>::bytes;
+  static constexpr int EPL = 16 / EB;                 // elements per lane per load
+  static constexpr int LPR = D / EPL;                 // lanes per row
+  static constexpr int RPI = 64 / LPR;                // rows per load instruction
+  static constexpr int NI = (G >= 8) ? 4 : 8;         // load instructions per chunk
+  static constexpr int NT = RPI * NI;                 // tokens per chunk
+  static constexpr int NV = NI * G;                   // partial dots per lane
+  static constexpr int R = NV >= LPR ? NV / LPR : 1;  // finished dots per lane
+  static constexpr int SLOTS = NT * G;                // logits per chunk
+  static constexpr int SPL = SLOTS >= 64 ? SLOTS / 64 : 1;
+  static_assert(LPR >= 2 && LPR <= 64, "row must span 2..64 lanes");
+  static_assert((G & (G - 1)) == 0 && G <= 64, "group size must be a power of two");
+};
+
+template <int DT, int D, int G>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+  using S = DecodeShape<DT, D, G>;
+  constexpr int EB = S::EB, EPL = S::EPL, LPR = S::LPR, RPI = S::RPI;
+  constexpr int NI = S::NI, NT = S::NT, NV = S::NV, R = S::R;
+  constexpr int SLOTS = S::SLOTS, SPL = S::SPL;
+
+  __shared__ float s_sc[kMaxWaves][SLOTS];
+  __shared__ float s_alpha[kMaxWaves][G];
+  __shared__ float s_m[kMaxWaves][G];
+  __shared__ float s_l[kMaxWaves][G];
+  __shared__ float s_acc[kMaxWaves][G * D];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  const int Hkv = p.num_kv_heads;
+  const int Hq = p.num_heads;
+  const int id = blockIdx.x;
+  const int g = id % Hkv;
+  const int rest = id / Hkv;
+  const int b = rest % p.num_seqs;
+  const int part = rest / p.num_seqs;
+
+  int L = p.context_lens[b];
+  L = min(L, p.max_context_len);
+  if (L <= 0) {
+    if (part == 0) {
+      for (int i = threadIdx.x; i < G * D; i += blockDim.x)
+        store_elem<DT>(p.out, ((size_t)b * Hq + (size_t)g * G) * D + i, 0.0f);
+    }
+    return;
+  }
+  const int P = p.part;
+  const int start = p.window > 0 ? max(0, L - p.window) : 0;
+  const int lo = max(start, part * P);
+  const int hi = min(L, part * P + P);
+  if (lo >= hi) return;
+  const bool single = (start / P) == ((L - 1) / P);
+
+  const int e0 = (lane % LPR) * EPL;  // first element of this lane's fragment
+  const int rsub = lane / LPR;        // row of this lane within a load
+
+  // query fragments of the G heads that read KV head g
+  uint4 qf[G];
+  {
+    const char* qb = static_cast<const char*>(p.q) +
+                     (((size_t)b * Hq + (size_t)g * G) * D + e0) * EB;
+#pragma unroll
+    for (int h = 0; h < G; ++h) qf[h] = ld16(qb + (size_t)h * D * EB);
+  }
+
+  // a window of 64 block-table entries, one per lane
+  const int32_t* bt = p.block_tables + (size_t)b * p.max_blocks_per_seq;
+  const int log2_bs = p.log2_bs;
+  const int last_pg = (hi - 1) >> log2_bs;
+  int pg0 = lo >> log2_bs;
+  int tbl = (pg0 + lane <= last_pg) ? bt[pg0 + lane] : 0;
+
+  const uint64_t row_bytes = (uint64_t)Hkv * D * EB;  // bytes between slots
+  const uint64_t lane_bytes = ((uint64_t)g * D + e0) * EB;
+  const char* kc = static_cast<const char*>(p.k_cache) + lane_bytes;
+  const char* vc = static_cast<const char*>(p.v_cache) + lane_bytes;
+
+  // physical slot (block * bs + offset) of each of this lane's rows in chunk c;
+  // positions outside [lo, hi) are clamped into it (their logits are masked
+  // later), so no unreferenced slot is ever read.
+  auto chunk_slots = [&](int c, uint32_t (&slot)[NI]) {
+    const int cs = c * NT;
+    const int cpg_hi = (min(cs + NT, hi) - 1) >> log2_bs;
+    if (cpg_hi - pg0 >= 64) {
+      pg0 = max(cs, lo) >> log2_bs;
+      tbl = (pg0 + lane <= last_pg) ? bt[pg0 + lane] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      int pos = cs + i * RPI + rsub;
+      pos = min(max(pos, lo), hi - 1);
+      int phys = __shfl(tbl, (pos >> log2_bs) - pg0, 64);
+      phys = ((unsigned)phys < (unsigned)p.num_blocks) ? phys : 0;
+      slot[i] = ((uint32_t)phys << log2_bs) | (uint32_t)(pos & ((1 << log2_bs) - 1));
+    }
+  };
+
+  const int c0 = lo / NT;
+  const int c1 = (hi - 1) / NT;
+  int c = c0 + w;
+
+  uint4 kr[NI], vr[NI];
+  uint32_t slot[NI];
+  if (c <= c1) {
+    chunk_slots(c, slot);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) kr[i] = ld16_stream(kc + slot[i] * row_bytes);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) vr[i] = ld16_stream(vc + slot[i] * row_bytes);
+  }
+
+  float m_run = kNegInf;  // running max (base 2) of query head lane % G
+  float l_run = 0.0f;     // this lane's share of that head's running sum
+  float acc[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
+
+  float* sc = s_sc[w];
+
+  for (; c <= c1; c += nw) {
+    const int cn = c + nw;
+    const bool has_next = cn <= c1;
+
+    // q.k partial sums over this lane's slice of each row
+    float dots[NV];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int h = 0; h < G; ++h) dots[i * G + h] = dot16<DT>(kr[i], qf[h], 0.0f);
+
+    // K of the next chunk goes in flight now
+    if (has_next) {
+      chunk_slots(cn, slot);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) kr[i] = ld16_stream(kc + slot[i] * row_bytes);
+    }
+
+    TransposeReduce<NV, LPR / 2, NV>::run(dots, lane);
+    const int jb = tr_base<NV, LPR>(lane);
+    const int cs = c * NT;
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+      const int j = jb + t;
+      const int row = (j / G) * RPI + rsub;
+      const int h = j % G;
+      const int pos = cs + row;
+      float s = dots[t];
+      s = p.cap_mul > 0.0f ? p.cap_mul * tanh_def(s * p.qk_mul) : s * p.qk_mul;
+      s = (pos >= lo && pos < hi) ? s : kNegInf;
+      sc[row * G + h] = s;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // online softmax: lane owns query head lane % G
+    float sv[SPL];
+    float cmax = kNegInf;
+#pragma unroll
+    for (int k = 0; k < SPL; ++k) {
+      const int idx = lane + 64 * k;
+      sv[k] = idx < SLOTS ? sc[idx] : kNegInf;
+      cmax = fmaxf(cmax, sv[k]);
+    }
+#pragma unroll
+    for (int m = G; m < 64; m <<= 1) cmax = fmaxf(cmax, shfl_xor_f(cmax, m));
+    const float m_new = fmaxf(m_run, cmax);
+    const float alpha = fast_exp2(m_run - m_new);
+    float psum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < SPL; ++k) {
+      const int idx = lane + 64 * k;
+      const float pk = fast_exp2(sv[k] - m_new);
+      psum += pk;
+      if (idx < SLOTS) sc[idx] = pk;
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    if (lane < G) s_alpha[w][lane] = alpha;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // P.V
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float a = s_alpha[w][h];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] *= a;
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float pr[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) pr[h] = sc[(i * RPI + rsub) * G + h];
+      float ve[EPL];
+      widen16<DT>(vr[i], ve);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pr[h], ve[e], acc[h][e]);
+    }
+    // V of the next chunk goes in flight
+    if (has_next) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) vr[i] = ld16_stream(vc + slot[i] * row_bytes);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- epilogue: finish this wavefront's sums, merge wavefronts in LDS ----
+#pragma unroll
+  for (int m = G; m < 64; m <<= 1) l_run += shfl_xor_f(l_run, m);
+#pragma unroll
+  for (int m = LPR; m < 64; m <<= 1)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] += shfl_xor_f(acc[h][e], m);
+  if (lane < G) {
+    s_m[w][lane] = m_run;
+    s_l[w][lane] = l_run;
+  }
+  if (lane < LPR) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_acc[w][h * D + e0 + e] = acc[h][e];
+  }
+  __syncthreads();
+
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+    const int h = i / D;
+    const int d = i % D;
+    float M = kNegInf;
+    for (int v = 0; v < nw; ++v) M = fmaxf(M, s_m[v][h]);
+    float den = 0.0f, num = 0.0f;
+    for (int v = 0; v < nw; ++v) {
+      const float f = fast_exp2(s_m[v][h] - M);
+      den += f * s_l[v][h];
+      num += f * s_acc[v][h * D + d];
+    }
+    const size_t hq = (size_t)g * G + h;
+    if (single) {
+      store_elem<DT>(p.out, ((size_t)b * Hq + hq) * D + d, num / den);
+    } else {
+      const size_t pi = ((size_t)b * Hq + hq) * p.num_parts + part;
+      p.tmp_out[pi * D + d] = num / den;
+      if (d == 0) {
+        p.max_logits[pi] = M;
+        p.exp_sums[pi] = den;
+      }
+    }
+  }
+}
+
+// One wavefront per (sequence, query head): merge the partials of sequences
+// that span more than one non-empty partition.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
+  constexpr int EPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
+  if (wid >= p.num_seqs * p.num_heads) return;
+  const int b = wid / p.num_heads;
+  const int hq = wid % p.num_heads;
+  int L = min(p.context_lens[b], p.max_context_len);
+  if (L <= 0) return;
+  const int P = p.part;
+  const int start = p.window > 0 ? max(0, L - p.window) : 0;
+  const int p0 = start / P;
+  const int p1 = (L - 1) / P;
+  if (p0 == p1) return;
+  const size_t base = ((size_t)b * p.num_heads + hq) * p.num_parts;
+
+  float M = kNegInf;
+  for (int q = p0 + lane; q <= p1; q += 64) M = fmaxf(M, p.max_logits[base + q]);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, shfl_xor_f(M, m));
+  float den = 0.0f;
+  for (int q = p0 + lane; q <= p1; q += 64)
+    den += p.exp_sums[base + q] * fast_exp2(p.max_logits[base + q] - M);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) den += shfl_xor_f(den, m);
+
+  float o[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = 0.0f;
+#pragma unroll 4
+  for (int q = p0; q <= p1; ++q) {
+    const float wq = p.exp_sums[base + q] * fast_exp2(p.max_logits[base + q] - M);
+    const float* src = p.tmp_out + (base + q) * D + lane * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] = fmaf(wq, src[e], o[e]);
+  }
+  const float inv = 1.0f / den;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e)
+    store_elem<DT>(p.out, ((size_t)b * p.num_heads + hq) * D + lane * EPL + e, o[e] * inv);
+}
+
+}  // namespace pa

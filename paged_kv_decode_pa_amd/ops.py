@@ -1,0 +1,148 @@
+"""Python binding over the C ABI (argument marshalling only).
+
+Tensors are used as device memory; every call is enqueued on torch's current
+HIP stream.  All arithmetic runs in the library's kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_DTYPE = {torch.float32: _lib.PA_F32, torch.float16: _lib.PA_F16,
+          torch.bfloat16: _lib.PA_BF16}
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _DTYPE[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("paged decode attention runs on the GPU: pass device tensors")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping) -> None:
+    """Write key[i]/value[i] ([T, Hkv, D]) into slot slot_mapping[i] (int64,
+    -1 = skip) of the paged caches ([NB, bs, Hkv, D]), in place."""
+    _dev(key, value, k_cache, v_cache, slot_mapping)
+    if slot_mapping.dtype != torch.int64:
+        raise TypeError("slot_mapping must be int64")
+    if not (key.dtype == value.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("key, value and caches must share a dtype")
+    NB, bs, Hkv, D = k_cache.shape
+    if tuple(v_cache.shape) != (NB, bs, Hkv, D):
+        raise ValueError("k_cache and v_cache shapes differ")
+    T = key.shape[0]
+    if tuple(key.shape) != (T, Hkv, D) or tuple(value.shape) != (T, Hkv, D) \
+            or tuple(slot_mapping.shape) != (T,):
+        raise ValueError("key/value must be [T, Hkv, D] and slot_mapping [T]")
+    lib = _lib.load()
+    _lib.check("pa_reshape_and_cache", lib.pa_reshape_and_cache(
+        key.data_ptr(), value.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        slot_mapping.data_ptr(), T, NB, bs, Hkv, D, _dt(key), _stream()))
+
+
+def partition_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                   max_context_len, window=0, dtype=torch.bfloat16) -> int:
+    """The library's choice of split-K partition size for a shape."""
+    return int(_lib.load().pa_decode_partition_size(
+        num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
+        window, _DTYPE[dtype]))
+
+
+def workspace_size(num_seqs, num_heads, head_dim, max_context_len, partition_size) -> int:
+    return int(_lib.load().pa_decode_workspace_size(
+        num_seqs, num_heads, head_dim, max_context_len, partition_size))
+
+
+def _shapes(q, k_cache, block_tables):
+    B, Hq, D = q.shape
+    NB, bs, Hkv, D2 = k_cache.shape
+    if D2 != D:
+        raise ValueError("head_dim of q and caches differ")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [num_seqs, max_blocks_per_seq]")
+    return B, Hq, D, NB, bs, Hkv
+
+
+def decode_partitions(out, workspace, q, k_cache, v_cache, block_tables, context_lens,
+                      max_context_len, scale, softcap, window, partition_size) -> None:
+    """pa_decode: the partition pass (writes `out` for single-partition
+    sequences and split-K partials to `workspace` for the others)."""
+    _dev(out, workspace, q, k_cache, v_cache, block_tables, context_lens)
+    B, Hq, D, NB, bs, Hkv = _shapes(q, k_cache, block_tables)
+    if context_lens.dtype != torch.int32 or tuple(context_lens.shape) != (B,):
+        raise ValueError("context_lens must be int32 [num_seqs]")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype == out.dtype):
+        raise TypeError("q, caches and out must share a dtype")
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must be [num_seqs, num_heads, head_dim]")
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    lib = _lib.load()
+    _lib.check("pa_decode", lib.pa_decode(
+        out.data_ptr(), ws_ptr, ws_bytes, q.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
+        context_lens.data_ptr(), int(max_context_len), B, Hq, Hkv, D, bs, NB,
+        float(scale), float(softcap), int(window), int(partition_size), _dt(q), _stream()))
+
+
+def decode_reduce(out, workspace, context_lens, max_context_len, partition_size,
+                  window) -> None:
+    """pa_decode_reduce: merge the partials of multi-partition sequences."""
+    _dev(out, workspace, context_lens)
+    B, Hq, D = out.shape
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    lib = _lib.load()
+    _lib.check("pa_decode_reduce", lib.pa_decode_reduce(
+        out.data_ptr(), ws_ptr, ws_bytes, context_lens.data_ptr(), int(max_context_len),
+        B, Hq, D, int(partition_size), int(window), _dt(out), _stream()))
+
+
+def alloc_workspace(num_seqs, num_heads, head_dim, max_context_len, partition_size,
+                    device) -> Optional[torch.Tensor]:
+    n = workspace_size(num_seqs, num_heads, head_dim, max_context_len, partition_size)
+    if n == 0:
+        return None
+    return torch.empty((n + 3) // 4, dtype=torch.float32, device=device)
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale, softcap=0.0, window=0,
+           partition_size=None, max_context_len=None, out=None, workspace=None):
+    """Paged decode attention: out[b, h] = softmax over the attended keys of
+    sequence b of (capped) scale * q[b, h] . k, applied to the values.
+
+    q [B, Hq, D]; k_cache/v_cache [NB, bs, Hkv, D]; block_tables int32
+    [B, max_blocks]; context_lens int32 [B] (counting the new token).
+    ``max_context_len`` defaults to context_lens.max() (one device sync).
+    """
+    B, Hq, D, NB, bs, Hkv = _shapes(q, k_cache, block_tables)
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if B else 0
+    if partition_size is None:
+        partition_size = globals()["partition_size"](B, Hq, Hkv, D, bs, max_context_len,
+                                                     window, q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = alloc_workspace(B, Hq, D, max_context_len, partition_size, q.device)
+    decode_partitions(out, workspace, q, k_cache, v_cache, block_tables, context_lens,
+                      max_context_len, scale, softcap, window, partition_size)
+    decode_reduce(out, workspace, context_lens, max_context_len, partition_size, window)
+    return out

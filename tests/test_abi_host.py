@@ -1,0 +1,129 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched):
+every symbol include/pa.h declares is exported, and every argument error is
+reported before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_decode_pa_amd as pa
+from paged_kv_decode_pa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert pa.status_string(0) == "ok"
+    for code in (-1, -2, -3, -4):
+        assert pa.status_string(code) not in ("ok", "unknown status")
+    assert pa.status_string(-99) == "unknown status"
+
+
+def test_workspace_size_arithmetic():
+    # [B, Hq, NP, D] fp32 + two [B, Hq, NP] fp32 arrays
+    B, Hq, D, L, P = 33, 32, 64, 131072, 512
+    NP = L // P
+    assert pa.workspace_size(B, Hq, D, L, P) == B * Hq * NP * (D + 2) * 4
+    assert pa.workspace_size(B, Hq, D, L, 0) == 0          # no split
+    assert pa.workspace_size(B, Hq, D, 300, 512) == 0      # one partition
+    assert pa.workspace_size(4, 8, 256, 513, 512) == 4 * 8 * 2 * 258 * 4
+
+
+def test_partition_choice_is_a_multiple_of_block_size():
+    for bs in (1, 16, 32):
+        for B, L in ((512, 1024), (16, 8192), (33, 131072), (4, 255)):
+            P = pa.partition_size(B, 8, 4, 256, bs, L)
+            assert P >= 0 and P % bs == 0
+
+
+def decode_args(**over):
+    a = dict(out=FAKE, ws=None, ws_bytes=0, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, maxb=8,
+             cl=FAKE, maxL=128, B=2, Hq=8, Hkv=2, D=64, bs=16, NB=64, scale=0.125,
+             softcap=0.0, window=0, P=0, dt=_lib.PA_F32, stream=None)
+    a.update(over)
+    return a
+
+
+def call_decode(a):
+    lib = _lib.load()
+    return lib.pa_decode(a["out"], a["ws"], a["ws_bytes"], a["q"], a["kc"], a["vc"], a["bt"],
+                         a["maxb"], a["cl"], a["maxL"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                         a["bs"], a["NB"], a["scale"], a["softcap"], a["window"], a["P"],
+                         a["dt"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(out=None), -1),
+    (dict(q=None), -1),
+    (dict(kc=None), -1),
+    (dict(bt=None), -1),
+    (dict(cl=None), -1),
+    (dict(Hq=6, Hkv=4), -1),              # heads not a multiple of kv heads
+    (dict(B=-1), -1),
+    (dict(maxL=129), -1),                 # more than max_blocks * block_size
+    (dict(P=24), -1),                     # not a multiple of block_size
+    (dict(P=-16), -1),
+    (dict(window=-1), -1),
+    (dict(softcap=-1.0), -1),
+    (dict(scale=float("nan")), -1),
+    (dict(D=96), -2),
+    (dict(dt=7), -2),
+    (dict(bs=12), -2),
+    (dict(Hq=32, Hkv=2), -2),             # group of 16 not built
+    (dict(Hq=6, Hkv=2), -2),              # group of 3 not built
+    (dict(P=16, maxL=128), -3),           # split needs a workspace
+    (dict(P=16, maxL=128, ws=FAKE, ws_bytes=100), -3),
+])
+def test_decode_rejects_bad_arguments(over, status):
+    assert call_decode(decode_args(**over)) == status
+
+
+def test_decode_with_no_sequences_is_a_noop():
+    assert call_decode(decode_args(B=0, out=None, q=None)) == 0
+
+
+def test_reduce_argument_checks():
+    lib = _lib.load()
+    # no split: nothing to reduce, nothing touched
+    assert lib.pa_decode_reduce(None, None, 0, None, 128, 2, 8, 64, 0, 0, 0, None) == 0
+    assert lib.pa_decode_reduce(FAKE, None, 0, FAKE, 128, 2, 8, 64, 16, 0, 0, None) == -3
+    assert lib.pa_decode_reduce(FAKE, FAKE, 10, FAKE, 128, 2, 8, 64, 16, 0, 0, None) == -3
+    assert lib.pa_decode_reduce(FAKE, FAKE, 1 << 20, FAKE, 128, 2, 8, 96, 16, 0, 0, None) == -2
+    assert lib.pa_decode_reduce(FAKE, FAKE, 1 << 20, FAKE, 128, 2, 8, 64, -1, 0, 0, None) == -1
+
+
+def test_reshape_argument_checks():
+    lib = _lib.load()
+    f = lib.pa_reshape_and_cache
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 16, 2, 64, 0, None) == 0   # no tokens
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 4, 64, 16, 2, 64, 0, None) == -1
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 4, 64, 16, 2, 64, 0, None) == -1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 64, 16, 2, 64, 0, None) == -1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 16, 2, 80, 0, None) == -2
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 3, 2, 64, 0, None) == -2
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 16, 2, 64, 5, None) == -2
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros(1, 2, 64)
+    with pytest.raises(ValueError):
+        pa.decode(q, torch.zeros(4, 16, 1, 64), torch.zeros(4, 16, 1, 64),
+                  torch.zeros(1, 1, dtype=torch.int32), torch.ones(1, dtype=torch.int32),
+                  0.125, max_context_len=1, partition_size=0)

@@ -1,0 +1,199 @@
+"""Decode attention on the GPU against the float64 oracle, element by element.
+
+Tolerance (max abs error): 1e-4 for float32 KV, 2e-2 for float16/bfloat16 KV
+(float32 accumulation, output rounded to the storage type).  Unreferenced
+blocks, the unused tail of every last block and block-table padding hold NaN
+or -1, so any read outside the attended keys poisons the result."""
+import numpy as np
+import pytest
+
+import oracle
+from workloads import gather_logical, assign_blocks, layout_cache, make_case, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu(case, **kw):
+    from gpu_util import DeviceCase, run_step, to_f64
+    return to_f64(run_step(DeviceCase(case), **kw))
+
+
+def check(case, got, seqs=None, tol=None):
+    from gpu_util import TOL
+    tol = TOL[case.dtype] if tol is None else tol
+    want = oracle.decode_case(case, seqs=seqs)
+    rows = slice(None) if seqs is None else list(seqs)
+    err = np.abs(got[rows] - want[rows])
+    assert np.isfinite(got[rows]).all(), "non-finite output"
+    assert err.max() <= tol, f"max abs err {err.max():.3g} > {tol}"
+    return float(err.max())
+
+
+# --------------------------------------------------------------------------
+# the five workloads
+# --------------------------------------------------------------------------
+def test_workload1_tiny_f32():
+    from gpu_util import say
+    say("workload 1")
+    c = workload(1)
+    for waves in (1, 2, 4):
+        check(c, gpu(c, waves=waves))
+
+
+@pytest.mark.parametrize("P", [None, 0, 128, 512])
+def test_workload2_gemma_global_with_new_rows(P):
+    from gpu_util import say
+    say(f"workload 2 P={P}")
+    c = workload(2)
+    check(c, gpu(c, partition_size=P))
+
+
+def test_workload3_gemma_sliding_window():
+    from gpu_util import say
+    say("workload 3")
+    c = workload(3)
+    check(c, gpu(c))
+
+
+@pytest.mark.parametrize("P", [None, 0, 256])
+def test_workload4_serving_b512(P):
+    from gpu_util import say
+    say(f"workload 4 P={P}")
+    c = workload(4)
+    got = gpu(c, partition_size=P)
+    L = c.context_lens
+    sample = sorted(set([int(np.argmin(L)), int(np.argmax(L))] +
+                        list(np.random.default_rng(0).choice(c.B, 40, replace=False))))
+    check(c, got, seqs=sample)
+
+
+def test_workload5_llama_long_context():
+    from gpu_util import say
+    say("workload 5")
+    c = workload(5)
+    got = gpu(c)
+    check(c, got, seqs=[32, 0, 7, 19, 31])
+
+
+# --------------------------------------------------------------------------
+# a matrix of small shapes: several chunks, ragged tails, every dtype
+# --------------------------------------------------------------------------
+SHAPES = [
+    # dtype, Hq, Hkv, D, bs, softcap, window, P
+    ("f32", 8, 2, 64, 16, 0.0, 0, 0),
+    ("f32", 4, 4, 128, 8, 30.0, 0, 64),
+    ("f32", 16, 2, 256, 32, 0.0, 50, 32),
+    ("f16", 32, 4, 64, 32, 0.0, 0, 64),
+    ("f16", 8, 8, 128, 16, 50.0, 70, 0),
+    ("f16", 16, 4, 256, 1, 0.0, 0, 48),
+    ("bf16", 8, 4, 256, 16, 50.0, 0, 0),
+    ("bf16", 8, 4, 256, 16, 50.0, 0, 64),
+    ("bf16", 8, 2, 128, 2, 20.0, 33, 16),
+    ("bf16", 32, 4, 64, 32, 0.0, 0, 32),
+    ("bf16", 32, 8, 128, 64, 0.0, 100, 128),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{s[0]}-g{s[1]//s[2]}-d{s[3]}-bs{s[4]}-c{s[5]:g}-w{s[6]}-p{s[7]}" for s in SHAPES])
+@pytest.mark.parametrize("waves", [1, 4])
+def test_small_shapes(shape, waves):
+    from gpu_util import say
+    dt, Hq, Hkv, D, bs, cap, W, P = shape
+    say(f"small {shape} waves={waves}")
+    L = [1, 2, 17, 100, 255, 513, 64, 31]
+    c = make_case(B=len(L), Hq=Hq, Hkv=Hkv, D=D, bs=bs, dtype=dt, context_lens=L,
+                  softcap=cap, window=W, partition_size=P, seed=sum(map(ord, str(shape))),
+                  extra_table_cols=3)
+    check(c, gpu(c, waves=waves))
+
+
+# --------------------------------------------------------------------------
+# invariants and edge cases on the GPU
+# --------------------------------------------------------------------------
+def test_single_key_is_exact():
+    from gpu_util import say
+    say("single key")
+    c = make_case(B=5, Hq=8, Hkv=4, D=256, bs=16, dtype="bf16", context_lens=[1] * 5,
+                  softcap=50.0, seed=3)
+    got = gpu(c)
+    want = oracle.decode_case(c)
+    assert np.array_equal(got, want)
+
+
+def test_window_one_is_exact():
+    from gpu_util import say
+    say("window one")
+    c = make_case(B=4, Hq=8, Hkv=2, D=128, bs=16, dtype="f16", context_lens=[3, 40, 200, 1000],
+                  window=1, seed=4, partition_size=64)
+    assert np.array_equal(gpu(c), oracle.decode_case(c))
+
+
+def test_empty_sequences_give_zero():
+    from gpu_util import say
+    say("empty sequences")
+    c = make_case(B=4, Hq=8, Hkv=4, D=64, bs=16, dtype="bf16", context_lens=[0, 30, 0, 600],
+                  seed=5, partition_size=128)
+    got = gpu(c)
+    assert np.all(got[[0, 2]] == 0)
+    check(c, got)
+
+
+def test_block_permutation_is_bit_identical():
+    from gpu_util import say
+    say("block permutation")
+    c = make_case(B=6, Hq=8, Hkv=4, D=256, bs=16, dtype="bf16",
+                  context_lens=[5, 77, 160, 300, 511, 1024], softcap=50.0, seed=6,
+                  partition_size=256)
+    a = gpu(c)
+    perm = np.random.default_rng(1).permutation(c.NB)
+    kc, vc = np.empty_like(c.k_cache), np.empty_like(c.v_cache)
+    kc[perm], vc[perm] = c.k_cache, c.v_cache
+    c.block_tables = np.where(c.block_tables >= 0, perm[np.maximum(c.block_tables, 0)],
+                              -1).astype(np.int32)
+    c.k_cache, c.v_cache = kc, vc
+    assert np.array_equal(gpu(c), a)
+
+
+def test_block_size_one_vs_sixteen():
+    from gpu_util import say
+    say("block size 1 vs 16")
+    c16 = make_case(B=3, Hq=8, Hkv=2, D=128, bs=16, dtype="bf16", context_lens=[9, 130, 400],
+                    softcap=50.0, seed=8, partition_size=0)
+    lk = gather_logical(c16.k_cache, c16.block_tables, c16.context_lens)
+    lv = gather_logical(c16.v_cache, c16.block_tables, c16.context_lens)
+    NB = sum(int(x) for x in c16.context_lens) + 3
+    bt = assign_blocks(c16.context_lens, 1, NB, np.random.default_rng(2))
+    c1 = make_case(B=3, Hq=8, Hkv=2, D=128, bs=1, dtype="bf16", context_lens=[9, 130, 400],
+                   softcap=50.0, seed=8, partition_size=0, NB=NB)
+    c1.q = c16.q
+    c1.block_tables = bt
+    c1.k_cache = layout_cache(lk, bt, NB, 1, "bf16")
+    c1.v_cache = layout_cache(lv, bt, NB, 1, "bf16")
+    a, b = gpu(c16), gpu(c1)
+    assert np.abs(a - b).max() <= 2e-2
+    check(c1, b)
+
+
+def test_gqa_head_map():
+    from gpu_util import say
+    say("gqa map")
+    c = make_case(B=3, Hq=32, Hkv=4, D=64, bs=32, dtype="f16", context_lens=[10, 99, 700],
+                  seed=9, partition_size=128)
+    for g in range(c.Hkv):
+        c.v_cache[:, :, g, :] = np.float16(g + 1).view(np.uint16)
+    got = gpu(c)
+    for h in range(c.Hq):
+        assert np.all(got[:, h, :] == h // 8 + 1)
+
+
+def test_output_guard_band_untouched():
+    import torch
+    from gpu_util import DeviceCase, run_step, say
+    say("guard band")
+    c = make_case(B=4, Hq=8, Hkv=4, D=256, bs=16, dtype="bf16", context_lens=[3, 60, 700, 1],
+                  seed=10, partition_size=128)
+    big = torch.full((c.B + 2, c.Hq, c.D), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = big[1:1 + c.B]
+    run_step(DeviceCase(c), out=out)
+    assert torch.all(big[0] == 7.0) and torch.all(big[-1] == 7.0)
+    check(c, out.float().cpu().numpy().astype(np.float64))

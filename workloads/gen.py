@@ -81,7 +81,7 @@ class Case:
     scale: float
     softcap: float             # <= 0: off
     window: int                # <= 0: off
-    partition_size: int        # 0: one partition per sequence
+    partition_size: Optional[int]  # 0: one partition per sequence; None: library's choice
     key: Optional[np.ndarray] = None           # [T, Hkv, D] storage, new rows
     value: Optional[np.ndarray] = None
     slot_mapping: Optional[np.ndarray] = None  # [T] int64, -1 = skip
@@ -203,7 +203,7 @@ def gather_logical(cache: np.ndarray, block_tables: np.ndarray, context_lens) ->
 def make_case(*, B: int, Hq: int, Hkv: int, D: int, bs: int, dtype: str,
               context_lens: Sequence[int], NB: Optional[int] = None,
               scale: Optional[float] = None, softcap: float = 0.0,
-              window: int = 0, partition_size: int = 0, seed: int = 0,
+              window: int = 0, partition_size: Optional[int] = 0, seed: int = 0,
               new_rows: bool = False, poison: bool = True,
               order: str = "shuffled", name: str = "custom",
               extra_table_cols: int = 0) -> Case:
@@ -257,7 +257,7 @@ def make_case(*, B: int, Hq: int, Hkv: int, D: int, bs: int, dtype: str,
     return Case(name=name, dtype=dtype, q=q, k_cache=kc, v_cache=vc,
                 block_tables=bt, context_lens=context_lens, scale=float(scale),
                 softcap=float(softcap), window=int(window),
-                partition_size=int(partition_size), key=key, value=value,
+                partition_size=partition_size, key=key, value=value,
                 slot_mapping=slots)
 
 
@@ -293,7 +293,9 @@ def workload_lengths(n: int) -> np.ndarray:
 
 
 def workload(n: int, poison: bool = True, partition_size: Optional[int] = None) -> Case:
-    """Workload n (1..5) at its full size."""
+    """Workload n (1..5) at its full size.  Workloads 1, 3 and 5 fix their
+    split (none; 512 tokens; 512 tokens); 2 and 4 leave it to the library
+    (None) unless ``partition_size`` is given."""
     L = workload_lengths(n)
     seed = 1000 + n
     if n == 1:
@@ -303,8 +305,7 @@ def workload(n: int, poison: bool = True, partition_size: Optional[int] = None) 
     elif n == 2:
         c = make_case(B=64, Hq=8, Hkv=4, D=256, bs=16, dtype="bf16", context_lens=L,
                       NB=8192, scale=1 / 16, softcap=50.0, seed=seed, new_rows=True,
-                      poison=poison,
-                      partition_size=0 if partition_size is None else partition_size)
+                      poison=poison, partition_size=partition_size)
     elif n == 3:
         c = make_case(B=16, Hq=8, Hkv=4, D=256, bs=16, dtype="bf16", context_lens=L,
                       scale=1 / 16, softcap=50.0, window=4096, seed=seed, poison=poison,
@@ -312,8 +313,7 @@ def workload(n: int, poison: bool = True, partition_size: Optional[int] = None) 
     elif n == 4:
         c = make_case(B=512, Hq=8, Hkv=4, D=256, bs=16, dtype="bf16", context_lens=L,
                       NB=40000, scale=1 / 16, softcap=50.0, seed=seed, poison=poison,
-                      new_rows=True,
-                      partition_size=0 if partition_size is None else partition_size)
+                      new_rows=True, partition_size=partition_size)
     elif n == 5:
         c = make_case(B=33, Hq=32, Hkv=4, D=64, bs=32, dtype="f16", context_lens=L,
                       scale=1 / 8, seed=seed, poison=poison,
