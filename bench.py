@@ -1,0 +1,282 @@
+"""Benchmark one paged-decode layer-step on one MI355X.
+
+A step is the whole hot path over one batch: reshape_and_cache of the batch's
+new K/V rows, pa_decode, and pa_decode_reduce when the library splits the
+keys.  The default workload is the high-concurrency serving step with
+Gemma-2-2B attention heads: 512 sequences, context = prompt U[16,512] +
+generated U[1,512] tokens, 8 query / 4 KV heads, head_dim 256, block_size 16,
+tanh soft-cap 50, bf16 KV, block tables drawn from a shuffled pool of 40000
+blocks.  Inputs are synthetic (seeded N(0,1)) and resident in HBM before the
+timed region starts.
+
+Prints ONE JSON line.  `value` is achieved HBM bandwidth of the whole step in
+GB/s, computed from the algorithmic bytes (K/V rows of attended tokens, q,
+out, block-table entries, context lengths, new rows) over the measured step
+time.  `roofline` reports the decode kernel alone: its algorithmic bytes over
+its average HIP-event-timed duration, against the 8 TB/s HBM peak.
+`cpu_baseline` times the float64 CPU oracle on a bounded sample of the same
+workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_decode_gemma2_b512_traffic.md")
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_decode_pa_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(digest: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("traffic:"):
+            for kv in line[len("traffic:"):].split():
+                k, _, v = kv.partition("=")
+                vals[k] = v
+    if vals.get("kernel_sources") != digest:
+        return None
+    try:
+        return float(vals["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(case, budget_s: float):
+    """Time the oracle on the workload's sequences, in order, until `budget_s`
+    seconds have been spent (whole passes over the batch are repeated when
+    one pass is shorter than the budget)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    eb = 2 if case.dtype != "f32" else 4
+    T = case.slot_mapping.shape[0] if case.slot_mapping is not None else 0
+    per_seq = case.attended().astype(np.int64) * case.Hkv * case.D * eb * 2 + 2 * case.Hq * case.D * eb + 4
+    L = case.context_lens.astype(np.int64)
+    n = case.attended().astype(np.int64)
+    per_seq += np.where(n > 0, (L - 1) // case.bs - (L - n) // case.bs + 1, 0) * 4
+    t0 = time.perf_counter()
+    seqs = passes = 0
+    bytes_ = 0
+    while seqs == 0 or time.perf_counter() - t0 < budget_s:
+        kc, vc = case.k_cache, case.v_cache
+        if T:
+            kc, vc = oracle.reshape_and_cache(case.key, case.value, kc, vc, case.slot_mapping)
+            bytes_ += 4 * T * case.Hkv * case.D * eb + 8 * T
+        for b in range(case.B):
+            oracle.decode(case.q, kc, vc, case.block_tables, case.context_lens, case.scale,
+                          case.softcap, case.window, case.dtype, seqs=[b])
+            bytes_ += int(per_seq[b])
+            seqs += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        passes += 1
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(bytes_ / dt / 1e9, 4), "unit": "GB/s",
+            "cores": blas_threads if blas_threads else cores,
+            "host_cores": cores, "kind": "oracle",
+            "seq_steps_per_s": round(seqs / dt, 2),
+            "sample": f"float64 numpy oracle on this workload: reshape_and_cache of its {T} new "
+                      f"rows then decode of its sequences in order, {seqs} sequence-steps over "
+                      f"{passes} pass(es) in {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="tokens per split-K partition (0 = none); default: library's choice")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--no-check", action="store_true", help="skip the parity spot-check")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the path needs no cross-GPU exchange and runs per GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_decode_pa_amd as pa
+    from workloads import WORKLOADS, workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    print(f"[bench] building workload {args.workload} ({WORKLOADS[args.workload]})", file=sys.stderr, flush=True)
+    case = workload(args.workload, partition_size=args.partition_size)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[case.dtype]
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(tdt)
+        return torch.from_numpy(a).to(dev)
+
+    q, kc, vc = up(case.q), up(case.k_cache), up(case.v_cache)
+    bt = torch.from_numpy(case.block_tables).to(dev)
+    cl = torch.from_numpy(case.context_lens).to(dev)
+    key = value = slots = None
+    if case.slot_mapping is not None:
+        key, value = up(case.key), up(case.value)
+        slots = torch.from_numpy(case.slot_mapping).to(dev)
+    B, Hq, D = case.q.shape
+    maxL = case.max_context_len
+    P = case.partition_size
+    if P is None:
+        P = pa.partition_size(B, Hq, case.Hkv, D, case.bs, maxL, case.window, tdt)
+    out = torch.empty_like(q)
+    ws = pa.alloc_workspace(B, Hq, D, maxL, P, dev)
+    split = pa.workspace_size(B, Hq, D, maxL, P) > 0
+    stream = torch.cuda.current_stream()
+
+    ev = []  # (before, after) pa_decode, per timed step
+
+    def step(record=False):
+        if slots is not None:
+            pa.reshape_and_cache(key, value, kc, vc, slots)
+        if record:
+            e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            e[0].record(stream)
+        pa.decode_partitions(out, ws, q, kc, vc, bt, cl, maxL, case.scale, case.softcap,
+                             case.window, P)
+        if record:
+            e[1].record(stream)
+            ev.append(e)
+        if split:
+            pa.decode_reduce(out, ws, cl, maxL, P, case.window)
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps; HIP events bracket each pa_decode launch
+    # on the stream it runs on (torch's current stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(record=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    decode_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    print(f"[bench] timed {args.steps} steps: {ms_step*1e3:.1f} us/step wall, "
+          f"pa_decode {decode_ms*1e3:.1f} us (HIP events)", file=sys.stderr, flush=True)
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy: 3 x {args.calib_copy_mib} MiB read + write",
+              file=sys.stderr, flush=True)
+
+    max_err = None
+    if not args.no_check:
+        import oracle
+        sample = sorted({int(np.argmax(case.context_lens)), int(np.argmin(case.context_lens)), 0, B - 1})
+        want = oracle.decode_case(case, seqs=sample)
+        got = out.float().cpu().numpy().astype(np.float64)
+        max_err = float(np.abs(got[sample] - want[sample]).max())
+        tol = 1e-4 if case.dtype == "f32" else 2e-2
+        print(f"[bench] parity spot-check on sequences {sample}: max abs err {max_err:.3e}",
+              file=sys.stderr, flush=True)
+        if not (max_err <= tol):
+            print("[bench] PARITY FAILURE", file=sys.stderr)
+            sys.exit(1)
+
+    ab = case.algorithmic_bytes()
+    step_s = ms_step / 1e3
+    value = ab["total"] / step_s / 1e9
+    achieved = ab["decode"] / (decode_ms / 1e3) / 1e9
+    digest = kernel_source_digest()
+    traffic = measured_traffic(digest)
+
+    cpu = None
+    if args.cpu_budget > 0:
+        print(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(case, args.cpu_budget)
+
+    dname = {"f32": "f32", "f16": "f16", "bf16": "bf16"}[case.dtype]
+    res = {
+        "metric": "paged decode attention: achieved HBM GB/s (% of peak) and seq-steps/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dname,
+        "data": "synthetic",
+        "config": {
+            "workload": case.name,
+            "num_seqs": B, "num_heads": Hq, "num_kv_heads": case.Hkv, "head_dim": D,
+            "block_size": case.bs, "num_blocks": case.NB, "softcap": case.softcap,
+            "window": case.window, "scale": case.scale,
+            "context_tokens": int(case.context_lens.sum()),
+            "max_context_len": maxL, "partition_size": P,
+            "new_rows": 0 if slots is None else int(slots.shape[0]),
+            "parallelism": "single GPU",
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "seq_steps_per_s": round(B / step_s, 1),
+        "us_per_layer_step": round(ms_step * 1e3, 2),
+        "algorithmic_bytes_per_step": ab["total"],
+        "pa_decode_us": round(decode_ms * 1e3, 2),
+        "split_k_reduce": bool(split),
+        "max_abs_err_vs_oracle": max_err,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "pa_decode",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": ab["decode"],
+            "kernel_sources": digest,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
