@@ -158,7 +158,7 @@ def main():
         P = pa.partition_size(B, Hq, case.Hkv, D, case.bs, maxL, case.window, tdt)
     out = torch.empty_like(q)
     ws = pa.alloc_workspace(B, Hq, D, maxL, P, dev)
-    split = pa.workspace_size(B, Hq, D, maxL, P) > 0
+    split = P > 0 and (maxL + P - 1) // P > 1
     stream = torch.cuda.current_stream()
 
     ev = []  # (before, after) pa_decode, per timed step

@@ -90,12 +90,14 @@ int pa_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads,
                              int window, pa_dtype dtype);
 
 /*
- * Bytes of workspace pa_decode needs for split-K partials:
+ * Bytes of workspace pa_decode needs (0 only when num_seqs <= 0):
+ *   order      [num_seqs] int32, padded to 256 bytes: the sequences sorted
+ *              longest first, written by pa_decode itself
+ * and, when the keys are split (partition_size > 0 and NP > 1), after it:
  *   tmp_out    [num_seqs, num_heads, NP, head_dim] float32
  *   max_logits [num_seqs, num_heads, NP]           float32 (base-2 logits)
  *   exp_sums   [num_seqs, num_heads, NP]           float32
- * with NP = ceil(max_context_len / partition_size).  0 when partition_size
- * is 0 or NP <= 1.  Host-only.
+ * with NP = ceil(max_context_len / partition_size).  Host-only.
  */
 size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim,
                                 int max_context_len, int partition_size);
@@ -103,8 +105,10 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim,
 /*
  * Decode attention, first pass.  The keys of each sequence are split at
  * absolute positions that are multiples of partition_size (0 = one partition
- * per sequence).  A sequence whose attended keys fall in a single partition
- * gets its output written to `out` directly; for the others each partition
+ * per sequence).  The workspace (pa_decode_workspace_size bytes) is
+ * required; its contents need no initialisation and are overwritten.  A
+ * sequence whose attended keys fall in a single partition gets its output
+ * written to `out` directly; for the others each partition
  * writes normalised partial outputs plus its running max and sum to the
  * workspace, and pa_decode_reduce must follow on the same stream.
  * An empty sequence (context_lens[b] == 0) gets out = 0.

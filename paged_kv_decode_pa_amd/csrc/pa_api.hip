@@ -8,6 +8,7 @@
 
 #include "../../include/pa.h"
 #include "pa_launch.h"
+#include "pa_plan.h"
 #include "pa_reshape.h"
 
 namespace {
@@ -109,13 +110,25 @@ int pa_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads, int 
   return part;
 }
 
-size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim, int max_context_len,
-                                int partition_size) {
-  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || partition_size <= 0) return 0;
+// Workspace layout: order [B] int32 (padded to 256 bytes), then, when the
+// keys are split, tmp_out [B,Hq,NP,D] f32, max_logits [B,Hq,NP] f32,
+// exp_sums [B,Hq,NP] f32.
+static size_t order_bytes(int num_seqs) { return ((size_t)num_seqs * 4 + 255) & ~(size_t)255; }
+
+static size_t partials_bytes(int num_seqs, int num_heads, int head_dim, int max_context_len,
+                             int partition_size) {
+  if (partition_size <= 0) return 0;
   const int np = num_parts(max_context_len, partition_size);
   if (np <= 1) return 0;
   const size_t rows = (size_t)num_seqs * num_heads * np;
   return rows * head_dim * sizeof(float) + 2 * rows * sizeof(float);
+}
+
+size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim, int max_context_len,
+                                int partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || partition_size < 0) return 0;
+  return order_bytes(num_seqs) +
+         partials_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size);
 }
 
 int pa_decode(void* out, void* workspace, size_t workspace_bytes, const void* q,
@@ -141,13 +154,14 @@ int pa_decode(void* out, void* workspace, size_t workspace_bytes, const void* q,
   const int np = num_parts(max_context_len, partition_size);
   const size_t need = pa_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
                                                partition_size);
-  if (need && (!workspace || workspace_bytes < need)) return PA_EWORKSPACE;
+  if (!workspace || workspace_bytes < need) return PA_EWORKSPACE;
 
   pa::DecodeParams p{};
   p.out = out;
-  if (need) {
+  p.order = static_cast<const int32_t*>(workspace);
+  if (partials_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size)) {
     const size_t rows = (size_t)num_seqs * num_heads * np;
-    float* ws = static_cast<float*>(workspace);
+    float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + order_bytes(num_seqs));
     p.tmp_out = ws;
     p.max_logits = ws + rows * head_dim;
     p.exp_sums = p.max_logits + rows;
@@ -182,12 +196,16 @@ int pa_decode(void* out, void* workspace, size_t workspace_bytes, const void* q,
   const long blocks = (long)num_seqs * num_kv_heads * np;
   if (blocks > 0x7fffffffL) return PA_EUNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  pa::plan_kernel<<<dim3(1), dim3(1024), 0, s>>>(context_lens, num_seqs, max_context_len, window,
+                                                static_cast<int32_t*>(workspace));
   const dim3 grid((unsigned)blocks), block(64 * nw);
+  // chunks of nt tokens stay inside one page when block_size >= nt
+  const bool paged = block_size >= nt;
   bool ok = false;
   switch (dtype) {
-    case PA_F32: ok = pa::launch_decode_f32(head_dim, G, grid, block, s, p); break;
-    case PA_F16: ok = pa::launch_decode_f16(head_dim, G, grid, block, s, p); break;
-    case PA_BF16: ok = pa::launch_decode_bf16(head_dim, G, grid, block, s, p); break;
+    case PA_F32: ok = pa::launch_decode_f32(head_dim, G, paged, grid, block, s, p); break;
+    case PA_F16: ok = pa::launch_decode_f16(head_dim, G, paged, grid, block, s, p); break;
+    case PA_BF16: ok = pa::launch_decode_bf16(head_dim, G, paged, grid, block, s, p); break;
   }
   if (!ok) return PA_EUNSUPPORTED;
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ELAUNCH;
@@ -200,14 +218,17 @@ int pa_decode_reduce(void* out, const void* workspace, size_t workspace_bytes,
   if (num_seqs < 0 || num_heads <= 0 || max_context_len < 0 || window < 0 || partition_size < 0)
     return PA_EINVAL;
   if (!valid_dtype(dtype) || !supported_head_dim(head_dim)) return PA_EUNSUPPORTED;
+  if (num_seqs == 0 ||
+      partials_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size) == 0)
+    return PA_OK;
+  if (!out || !context_lens) return PA_EINVAL;
   const size_t need = pa_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
                                                partition_size);
-  if (num_seqs == 0 || need == 0) return PA_OK;
-  if (!out || !context_lens) return PA_EINVAL;
   if (!workspace || workspace_bytes < need) return PA_EWORKSPACE;
   const int np = num_parts(max_context_len, partition_size);
   const size_t rows = (size_t)num_seqs * num_heads * np;
-  const float* ws = static_cast<const float*>(workspace);
+  const float* ws = reinterpret_cast<const float*>(static_cast<const char*>(workspace) +
+                                                   order_bytes(num_seqs));
   pa::ReduceParams p{};
   p.out = out;
   p.tmp_out = ws;

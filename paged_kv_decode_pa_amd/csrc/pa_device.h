@@ -39,6 +39,19 @@ __device__ __forceinline__ uint4 ld16_stream(const void* p) {
   return r;
 }
 
+// Buffer descriptor over [base, base + bytes): loads through it take a
+// wave-uniform base in scalar registers plus a 32-bit per-lane offset, and
+// return 0 instead of touching memory outside the range.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                          0x00020000);
+}
+// 16-byte streaming (non-temporal) buffer load at base + soff + voff.
+__device__ __forceinline__ uint4 ld16_buf(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 2));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float f16_lo(uint32_t w) {
@@ -150,7 +163,25 @@ __device__ __forceinline__ float tanh_def(float x) {
 // ---------------------------------------------------------------------------
 // wavefront reductions
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+__device__ __forceinline__ int lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+// v from lane (lane ^ mask).  Masks 1, 2 and 8 stay inside a 16-lane row
+// and use DPP (quad permute, row rotate by 8); 4 and 16 use the LDS-free
+// swizzle network; 32 uses the lane permute crossbar.  `mask` is a
+// compile-time constant after unrolling, so the chain folds to one case.
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+  const int x = __float_as_int(v);
+  int r;
+  if (mask == 1) r = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);        // quad_perm 1,0,3,2
+  else if (mask == 2) r = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+  else if (mask == 8) r = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row_ror 8
+  else if (mask == 4) r = __builtin_amdgcn_ds_swizzle(x, 0x1F | (4 << 10));
+  else if (mask == 16) r = __builtin_amdgcn_ds_swizzle(x, 0x1F | (16 << 10));
+  else r = __builtin_amdgcn_ds_bpermute((lane_id() ^ mask) << 2, x);
+  return __int_as_float(r);
+}
 
 // Reduce-scatter of N independent partial sums across the LPR lanes of an
 // aligned lane group.  Step by step (masks LPR/2 .. 1) each lane keeps half

@@ -21,6 +21,8 @@
 // keeps a chunk of K and V in flight while it computes.
 #pragma once
 
+#include <type_traits>
+
 #include "pa_device.h"
 
 namespace pa {
@@ -29,6 +31,7 @@ constexpr int kMaxWaves = 4;
 
 struct DecodeParams {
   void* out;               // [B, Hq, D]
+  const int32_t* order;    // [B] sequences, longest first (workspace)
   float* tmp_out;          // [B, Hq, NP, D]
   float* max_logits;       // [B, Hq, NP], base-2 logits
   float* exp_sums;         // [B, Hq, NP]
@@ -81,8 +84,15 @@ struct DecodeShape {
   static_assert((G & (G - 1)) == 0 && G <= 64, "group size must be a power of two");
 };
 
-template <int DT, int D, int G>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+// PAGED: every chunk lies inside one KV page (block_size >= NT), so a
+// chunk's rows share one physical block: its base address is wave-uniform
+// (scalar registers) and each lane adds a 32-bit row offset.  Otherwise each
+// row looks up its own block.
+#ifndef PA_DECODE_MIN_WAVES
+#define PA_DECODE_MIN_WAVES 1
+#endif
+template <int DT, int D, int G, bool PAGED>
+__global__ __launch_bounds__(256, PA_DECODE_MIN_WAVES) void decode_kernel(DecodeParams p) {
   using S = DecodeShape<DT, D, G>;
   constexpr int EB = S::EB, EPL = S::EPL, LPR = S::LPR, RPI = S::RPI;
   constexpr int NI = S::NI, NT = S::NT, NV = S::NV, R = S::R;
@@ -93,6 +103,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   __shared__ float s_m[kMaxWaves][G];
   __shared__ float s_l[kMaxWaves][G];
   __shared__ float s_acc[kMaxWaves][G * D];
+  __shared__ int32_t s_tbl[kMaxWaves][64];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -102,8 +113,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   const int id = blockIdx.x;
   const int g = id % Hkv;
   const int rest = id / Hkv;
-  const int b = rest % p.num_seqs;
   const int part = rest / p.num_seqs;
+  // workgroups are dispatched in index order: taking sequences longest
+  // first leaves the short ones to fill in at the end
+  const int b = ((const __attribute__((address_space(4))) int32_t*)p.order)[rest % p.num_seqs];
 
   int L = p.context_lens[b];
   L = min(L, p.max_context_len);
@@ -133,51 +146,95 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     for (int h = 0; h < G; ++h) qf[h] = ld16(qb + (size_t)h * D * EB);
   }
 
-  // a window of 64 block-table entries, one per lane
+  // A window of 64 consecutive block-table entries per wavefront, in LDS.
+  // Refilled (rarely: every 64 pages) inside a uniform branch, so the wait
+  // for the refill never holds back the K/V loads already in flight.
   const int32_t* bt = p.block_tables + (size_t)b * p.max_blocks_per_seq;
   const int log2_bs = p.log2_bs;
   const int last_pg = (hi - 1) >> log2_bs;
-  int pg0 = lo >> log2_bs;
-  int tbl = (pg0 + lane <= last_pg) ? bt[pg0 + lane] : 0;
-
-  const uint64_t row_bytes = (uint64_t)Hkv * D * EB;  // bytes between slots
-  const uint64_t lane_bytes = ((uint64_t)g * D + e0) * EB;
-  const char* kc = static_cast<const char*>(p.k_cache) + lane_bytes;
-  const char* vc = static_cast<const char*>(p.v_cache) + lane_bytes;
-
-  // physical slot (block * bs + offset) of each of this lane's rows in chunk c;
-  // positions outside [lo, hi) are clamped into it (their logits are masked
-  // later), so no unreferenced slot is ever read.
-  auto chunk_slots = [&](int c, uint32_t (&slot)[NI]) {
-    const int cs = c * NT;
-    const int cpg_hi = (min(cs + NT, hi) - 1) >> log2_bs;
-    if (cpg_hi - pg0 >= 64) {
-      pg0 = max(cs, lo) >> log2_bs;
-      tbl = (pg0 + lane <= last_pg) ? bt[pg0 + lane] : 0;
-    }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      int pos = cs + i * RPI + rsub;
-      pos = min(max(pos, lo), hi - 1);
-      int phys = __shfl(tbl, (pos >> log2_bs) - pg0, 64);
-      phys = ((unsigned)phys < (unsigned)p.num_blocks) ? phys : 0;
-      slot[i] = ((uint32_t)phys << log2_bs) | (uint32_t)(pos & ((1 << log2_bs) - 1));
-    }
+  int32_t* tbl = s_tbl[w];
+  int pg0 = -(1 << 30);
+  auto refill = [&](int first) {
+    pg0 = first;
+    const int pg = first + lane;
+    const int v = pg <= last_pg ? bt[pg] : 0;
+    tbl[lane] = v;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  const int c0 = lo / NT;
-  const int c1 = (hi - 1) / NT;
-  int c = c0 + w;
+  const uint32_t row_bytes = (uint32_t)(Hkv * D * EB);          // bytes between slots
+  const uint32_t lane_bytes = (uint32_t)((g * D + e0) * EB);
+  const uint32_t page_bytes = row_bytes << log2_bs;
+  const char* kbase = static_cast<const char*>(p.k_cache);
+  const char* vbase = static_cast<const char*>(p.v_cache);
+  // harmless L2-resident target for the prefetch slot of the last chunk
+  const char* dummy = static_cast<const char*>(p.q) + ((size_t)b * Hq + (size_t)g * G) * D * EB;
+  const uint32_t dummy_off = (uint32_t)(e0 * EB);
 
-  uint4 kr[NI], vr[NI];
-  uint32_t slot[NI];
-  if (c <= c1) {
-    chunk_slots(c, slot);
+  // Chunk c covers positions [c*NT, c*NT + NT).  Rows outside [lo, hi) are
+  // clamped into it (their logits are masked later), so no unreferenced slot
+  // (free block, page tail, table padding) is ever read.
+  //   PAGED: one buffer descriptor per page (scalar registers), the chunk's
+  //          offset in the page as the scalar offset, 32-bit row offsets;
+  //   else:  per-row slot index (block * bs + offset), 64-bit addresses.
+  struct Addr {
+    rsrc_t kr, vr;
+    uint32_t soff;
+    uint32_t off[NI];
+  };
+  auto page_addr = [&](int c, int phys, Addr& a) {
+    const int cs = c * NT;
+    phys = ((unsigned)phys < (unsigned)p.num_blocks) ? phys : 0;
+    const uint64_t base = (uint64_t)phys * page_bytes;
+    a.kr = make_rsrc(kbase + base, page_bytes);
+    a.vr = make_rsrc(vbase + base, page_bytes);
+    a.soff = (uint32_t)(cs & ((1 << log2_bs) - 1)) * row_bytes;
+    const int rlo = lo - cs, rhi = hi - 1 - cs;  // uniform clamp bounds
 #pragma unroll
-    for (int i = 0; i < NI; ++i) kr[i] = ld16_stream(kc + slot[i] * row_bytes);
+    for (int i = 0; i < NI; ++i) {
+      const int r = min(max(i * RPI + rsub, rlo), rhi);
+      a.off[i] = (uint32_t)r * row_bytes + lane_bytes;
+    }
+  };
+  auto chunk_addr = [&](int c, Addr& a) {
+    const int cs = c * NT;
+    const int cpg_lo = max(cs, lo) >> log2_bs;
+    const int cpg_hi = (min(cs + NT, hi) - 1) >> log2_bs;
+    if (cpg_lo < pg0 || cpg_hi - pg0 >= 64) refill(cpg_lo);
+    if constexpr (PAGED) {
+      page_addr(c, __builtin_amdgcn_readfirstlane(tbl[cpg_lo - pg0]), a);
+    } else {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) vr[i] = ld16_stream(vc + slot[i] * row_bytes);
-  }
+      for (int i = 0; i < NI; ++i) {
+        const int pos = min(max(cs + i * RPI + rsub, lo), hi - 1);
+        int phys = tbl[(pos >> log2_bs) - pg0];
+        phys = ((unsigned)phys < (unsigned)p.num_blocks) ? phys : 0;
+        a.off[i] = ((uint32_t)phys << log2_bs) | (uint32_t)(pos & ((1 << log2_bs) - 1));
+      }
+    }
+  };
+  auto kload = [&](const Addr& a, int i) -> uint4 {
+    if constexpr (PAGED) return ld16_buf(a.kr, a.off[i], a.soff);
+    else return ld16_stream(kbase + (uint64_t)a.off[i] * row_bytes + lane_bytes);
+  };
+  auto vload = [&](const Addr& a, int i) -> uint4 {
+    if constexpr (PAGED) return ld16_buf(a.vr, a.off[i], a.soff);
+    else return ld16_stream(vbase + (uint64_t)a.off[i] * row_bytes + lane_bytes);
+  };
+  auto dummy_addr = [&](Addr& a) {
+    if constexpr (PAGED) {
+      a.kr = make_rsrc(dummy, (uint32_t)(G * D * EB));
+      a.vr = a.kr;
+      a.soff = 0;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) a.off[i] = dummy_off;
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) a.off[i] = 0;
+    }
+  };
 
   float m_run = kNegInf;  // running max (base 2) of query head lane % G
   float l_run = 0.0f;     // this lane's share of that head's running sum
@@ -188,11 +245,46 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
 
   float* sc = s_sc[w];
+  uint4 kr[NI], vr[NI];
+  Addr ad;
 
+  const int c0 = lo / NT;
+  const int c1 = (hi - 1) / NT;
+  int c = c0 + w;
+  if (c <= c1) {
+    if constexpr (PAGED) {
+      // first chunk: its block id through the scalar cache, so K/V loads
+      // start before the block-table window arrives
+      typedef const __attribute__((address_space(4))) int32_t cint32;
+      const int cpg = max(c * NT, lo) >> log2_bs;
+      page_addr(c, ((cint32*)bt)[cpg], ad);
+      pg0 = cpg;
+      const int v = cpg + lane <= last_pg ? bt[cpg + lane] : 0;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) kr[i] = kload(ad, i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) vr[i] = vload(ad, i);
+      __builtin_amdgcn_sched_barrier(0);
+      tbl[lane] = v;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+      chunk_addr(c, ad);
+      // issue all of K before any of V, as the loop does: the wait counter
+      // then lets q.k start while V is still in flight
+#pragma unroll
+      for (int i = 0; i < NI; ++i) kr[i] = kload(ad, i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) vr[i] = vload(ad, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+#pragma clang loop unroll(disable)
   for (; c <= c1; c += nw) {
-    const int cn = c + nw;
-    const bool has_next = cn <= c1;
-
     // q.k partial sums over this lane's slice of each row
     float dots[NV];
 #pragma unroll
@@ -200,12 +292,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int h = 0; h < G; ++h) dots[i * G + h] = dot16<DT>(kr[i], qf[h], 0.0f);
 
-    // K of the next chunk goes in flight now
-    if (has_next) {
-      chunk_slots(cn, slot);
+    // the next chunk's K goes in flight (the last chunk re-reads a few
+    // L2-resident bytes instead, so the loads stay unconditional)
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + nw <= c1) chunk_addr(c + nw, ad);
+    else dummy_addr(ad);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) kr[i] = ld16_stream(kc + slot[i] * row_bytes);
-    }
+    for (int i = 0; i < NI; ++i) kr[i] = kload(ad, i);
+    __builtin_amdgcn_sched_barrier(0);
 
     TransposeReduce<NV, LPR / 2, NV>::run(dots, lane);
     const int jb = tr_base<NV, LPR>(lane);
@@ -272,11 +366,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pr[h], ve[e], acc[h][e]);
     }
-    // V of the next chunk goes in flight
-    if (has_next) {
+    // the next chunk's V goes in flight
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) vr[i] = ld16_stream(vc + slot[i] * row_bytes);
-    }
+    for (int i = 0; i < NI; ++i) vr[i] = vload(ad, i);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
   }

@@ -36,13 +36,16 @@ def test_status_strings():
 
 
 def test_workspace_size_arithmetic():
-    # [B, Hq, NP, D] fp32 + two [B, Hq, NP] fp32 arrays
+    # order [B] int32 padded to 256 B, then [B, Hq, NP, D] fp32 + two [B, Hq, NP] fp32
+    def order(B):
+        return (B * 4 + 255) // 256 * 256
     B, Hq, D, L, P = 33, 32, 64, 131072, 512
     NP = L // P
-    assert pa.workspace_size(B, Hq, D, L, P) == B * Hq * NP * (D + 2) * 4
-    assert pa.workspace_size(B, Hq, D, L, 0) == 0          # no split
-    assert pa.workspace_size(B, Hq, D, 300, 512) == 0      # one partition
-    assert pa.workspace_size(4, 8, 256, 513, 512) == 4 * 8 * 2 * 258 * 4
+    assert pa.workspace_size(B, Hq, D, L, P) == order(B) + B * Hq * NP * (D + 2) * 4
+    assert pa.workspace_size(B, Hq, D, L, 0) == order(B)          # no split
+    assert pa.workspace_size(B, Hq, D, 300, 512) == order(B)      # one partition
+    assert pa.workspace_size(4, 8, 256, 513, 512) == 256 + 4 * 8 * 2 * 258 * 4
+    assert pa.workspace_size(0, 8, 256, 513, 512) == 0
 
 
 def test_partition_choice_is_a_multiple_of_block_size():
@@ -87,8 +90,9 @@ def call_decode(a):
     (dict(bs=12), -2),
     (dict(Hq=32, Hkv=2), -2),             # group of 16 not built
     (dict(Hq=6, Hkv=2), -2),              # group of 3 not built
-    (dict(P=16, maxL=128), -3),           # split needs a workspace
-    (dict(P=16, maxL=128, ws=FAKE, ws_bytes=100), -3),
+    (dict(P=16, maxL=128), -3),           # no workspace
+    (dict(P=0, maxL=128), -3),            # the work order needs one too
+    (dict(P=16, maxL=128, ws=FAKE, ws_bytes=300), -3),
 ])
 def test_decode_rejects_bad_arguments(over, status):
     assert call_decode(decode_args(**over)) == status
