@@ -58,6 +58,12 @@ int chunk_tokens(int dt, int D, int G) {
   return rpi * ni;
 }
 
+// LDS bytes one decode wavefront uses (DecodeShape::LDS_FLOATS).
+size_t decode_lds_bytes(int dt, int D, int G) {
+  const int slots = chunk_tokens(dt, D, G) * G;
+  return sizeof(float) * (size_t)(slots + G + 64 + 2 * G + G * D);
+}
+
 }  // namespace
 
 extern "C" {
@@ -145,7 +151,11 @@ int pa_decode(void* out, void* workspace, size_t workspace_bytes, const void* q,
   if (!valid_dtype(dtype) || !supported_head_dim(head_dim) || !pow2_in(block_size, 1, 256))
     return PA_EUNSUPPORTED;
   const int G = num_heads / num_kv_heads;
-  if (!(G == 1 || G == 2 || G == 4 || G == 8)) return PA_EUNSUPPORTED;
+  // matrix cores take groups of 8 or 16 heads over 16-bit KV whose chunks
+  // of 16 or 32 tokens fit in a page; PA_DECODE_MFMA=0 forces the vector path
+  const bool mfma = (dtype == PA_F16 || dtype == PA_BF16) && (G == 8 || G == 16) &&
+                    block_size >= 16 && env_int("PA_DECODE_MFMA", 1) != 0;
+  if (!(G == 1 || G == 2 || G == 4 || G == 8 || (G == 16 && mfma))) return PA_EUNSUPPORTED;
   if (partition_size > 0 && partition_size % block_size) return PA_EINVAL;
   if ((long)max_context_len > (long)max_blocks_per_seq * block_size) return PA_EINVAL;
   if (num_seqs == 0) return PA_OK;
@@ -189,10 +199,16 @@ int pa_decode(void* out, void* workspace, size_t workspace_bytes, const void* q,
     p.cap_mul = 0.0f;
   }
 
-  const int nt = chunk_tokens(dtype, head_dim, G);
+  // two 16-token tiles per chunk when pages hold 32+ tokens and the K
+  // fragments of both fit in registers (head_dim <= 128)
+  const int tiles = block_size >= 32 && head_dim <= 128 ? 2 : 1;
+  const int nt = mfma ? 16 * tiles : chunk_tokens(dtype, head_dim, G);
+  const size_t lds_wave = mfma ? pa::decode_mfma_lds_bytes(head_dim, G, tiles)
+                               : decode_lds_bytes(dtype, head_dim, G);
   const int span = window > 0 && window < p.part ? window : p.part;
   const long units = (long)num_seqs * num_kv_heads * np;
-  const int nw = waves_for(span, nt, (int)(units < (1L << 30) ? units : (1L << 30)));
+  int nw = waves_for(span, nt, (int)(units < (1L << 30) ? units : (1L << 30)));
+  while (nw > 1 && nw * lds_wave > 65536) nw /= 2;
   const long blocks = (long)num_seqs * num_kv_heads * np;
   if (blocks > 0x7fffffffL) return PA_EUNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -202,10 +218,15 @@ int pa_decode(void* out, void* workspace, size_t workspace_bytes, const void* q,
   // chunks of nt tokens stay inside one page when block_size >= nt
   const bool paged = block_size >= nt;
   bool ok = false;
-  switch (dtype) {
-    case PA_F32: ok = pa::launch_decode_f32(head_dim, G, paged, grid, block, s, p); break;
-    case PA_F16: ok = pa::launch_decode_f16(head_dim, G, paged, grid, block, s, p); break;
-    case PA_BF16: ok = pa::launch_decode_bf16(head_dim, G, paged, grid, block, s, p); break;
+  if (mfma) {
+    ok = dtype == PA_F16 ? pa::launch_decode_mfma_f16(head_dim, G, tiles, nw, grid, s, p)
+                         : pa::launch_decode_mfma_bf16(head_dim, G, tiles, nw, grid, s, p);
+  } else {
+    switch (dtype) {
+      case PA_F32: ok = pa::launch_decode_f32(head_dim, G, paged, grid, block, s, p); break;
+      case PA_F16: ok = pa::launch_decode_f16(head_dim, G, paged, grid, block, s, p); break;
+      case PA_BF16: ok = pa::launch_decode_bf16(head_dim, G, paged, grid, block, s, p); break;
+    }
   }
   if (!ok) return PA_EUNSUPPORTED;
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ELAUNCH;
@@ -241,8 +262,9 @@ int pa_decode_reduce(void* out, const void* workspace, size_t workspace_bytes,
   p.window = window;
   p.part = partition_size;
   p.num_parts = np;
-  const long waves = (long)num_seqs * num_heads;
-  const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  const long groups = (long)num_seqs * num_heads;
+  if (groups > 0x7fffffffL) return PA_EUNSUPPORTED;
+  const dim3 grid((unsigned)groups), block(256);
   hipStream_t s = static_cast<hipStream_t>(stream);
 #define PA_REDUCE_CASE(DTV, DT)                                                   \
   case DTV:                                                                       \

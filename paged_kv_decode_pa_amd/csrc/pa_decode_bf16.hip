@@ -3,4 +3,5 @@
 
 namespace pa {
 PA_DEFINE_DECODE_LAUNCHER(launch_decode_bf16, DT_BF16)
+PA_DEFINE_MFMA_LAUNCHER(launch_decode_mfma_bf16, DT_BF16)
 }  // namespace pa

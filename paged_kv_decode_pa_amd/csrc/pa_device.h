@@ -52,6 +52,13 @@ __device__ __forceinline__ uint4 ld16_buf(rsrc_t r, uint32_t voff, uint32_t soff
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 2));
 }
 
+// 16-byte streaming buffer load written straight into LDS: lane l's bytes
+// land at lds + 16*l (the address is wave-uniform and goes through M0).
+__device__ __forceinline__ void ld16_buf_to_lds(rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           (int)voff, (int)soff, 0, 2);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float f16_lo(uint32_t w) {

@@ -2,7 +2,7 @@
 // partition reduce and the KV-cache scatter.
 //
 // Decode work unit: one workgroup per (sequence b, KV head g, partition p),
-// with 1..4 wavefronts that take the partition's chunks round-robin and are
+// with 1..8 wavefronts that take the partition's chunks round-robin and are
 // merged in LDS at the end.  Within a wavefront:
 //   * a K/V row of head g (D elements) is spread over LPR lanes, 16 bytes
 //     per lane, so one load instruction fetches RPI = 64/LPR whole rows and a
@@ -27,7 +27,7 @@
 
 namespace pa {
 
-constexpr int kMaxWaves = 4;
+constexpr int kMaxWaves = 8;
 
 struct DecodeParams {
   void* out;               // [B, Hq, D]
@@ -80,9 +80,79 @@ struct DecodeShape {
   static constexpr int R = NV >= LPR ? NV / LPR : 1;  // finished dots per lane
   static constexpr int SLOTS = NT * G;                // logits per chunk
   static constexpr int SPL = SLOTS >= 64 ? SLOTS / 64 : 1;
+  // LDS floats per wavefront: logits, rescale, table window, max/sum, acc
+  static constexpr int LDS_FLOATS = SLOTS + G + 64 + 2 * G + G * D;
   static_assert(LPR >= 2 && LPR <= 64, "row must span 2..64 lanes");
   static_assert((G & (G - 1)) == 0 && G <= 64, "group size must be a power of two");
 };
+
+// The (sequence, KV head, partition) unit of a decode workgroup.
+struct Unit {
+  int b, g, part, lo, hi;
+  bool single;  // the sequence's attended keys fall in this one partition
+};
+
+// Decodes blockIdx into a unit: KV head fastest, then sequences in the
+// plan's longest-first order, then partitions (so a sequence's partitions
+// are spread over the whole dispatch).  Returns false when the workgroup has
+// no keys to attend to; partition 0 of an empty sequence writes its zero
+// output.
+template <int DT, int D, int G>
+__device__ __forceinline__ bool decode_unit(const DecodeParams& p, Unit& u) {
+  typedef const __attribute__((address_space(4))) int32_t cint32;
+  const int id = blockIdx.x;
+  u.g = id % p.num_kv_heads;
+  const int rest = id / p.num_kv_heads;
+  u.part = rest / p.num_seqs;
+  u.b = ((cint32*)p.order)[rest % p.num_seqs];
+  const int L = min(p.context_lens[u.b], p.max_context_len);
+  if (L <= 0) {
+    if (u.part == 0)
+      for (int i = threadIdx.x; i < G * D; i += blockDim.x)
+        store_elem<DT>(p.out, ((size_t)u.b * p.num_heads + (size_t)u.g * G) * D + i, 0.0f);
+    return false;
+  }
+  const int P = p.part;
+  const int start = p.window > 0 ? max(0, L - p.window) : 0;
+  u.lo = max(start, u.part * P);
+  u.hi = min(L, u.part * P + P);
+  u.single = (start / P) == ((L - 1) / P);
+  return u.lo < u.hi;
+}
+
+// Merges the wavefronts' running (max, sum, accumulators) and writes the
+// unit's G output rows, or its split-K partials.  Wavefront v's record
+// starts at smem + v * stride: maxima at +ml, sums at +ml + G, accumulators
+// [G][D] at +acc.
+template <int DT, int D, int G>
+__device__ __forceinline__ void merge_store(const DecodeParams& p, const Unit& u,
+                                            const float* smem, int stride, int ml, int acc,
+                                            int nw) {
+  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
+    const int h = i / D;
+    const int d = i % D;
+    float M = kNegInf;
+    for (int v = 0; v < nw; ++v) M = fmaxf(M, smem[v * stride + ml + h]);
+    float den = 0.0f, num = 0.0f;
+    for (int v = 0; v < nw; ++v) {
+      const float* lv = smem + v * stride;
+      const float f = fast_exp2(lv[ml + h] - M);
+      den += f * lv[ml + G + h];
+      num += f * lv[acc + h * D + d];
+    }
+    const size_t hq = (size_t)u.g * G + h;
+    if (u.single) {
+      store_elem<DT>(p.out, ((size_t)u.b * p.num_heads + hq) * D + d, num / den);
+    } else {
+      const size_t pi = ((size_t)u.b * p.num_heads + hq) * p.num_parts + u.part;
+      p.tmp_out[pi * D + d] = num / den;
+      if (d == 0) {
+        p.max_logits[pi] = M;
+        p.exp_sums[pi] = den;
+      }
+    }
+  }
+}
 
 // PAGED: every chunk lies inside one KV page (block_size >= NT), so a
 // chunk's rows share one physical block: its base address is wave-uniform
@@ -92,47 +162,29 @@ struct DecodeShape {
 #define PA_DECODE_MIN_WAVES 1
 #endif
 template <int DT, int D, int G, bool PAGED>
-__global__ __launch_bounds__(256, PA_DECODE_MIN_WAVES) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64 * kMaxWaves, PA_DECODE_MIN_WAVES) void decode_kernel(DecodeParams p) {
   using S = DecodeShape<DT, D, G>;
   constexpr int EB = S::EB, EPL = S::EPL, LPR = S::LPR, RPI = S::RPI;
   constexpr int NI = S::NI, NT = S::NT, NV = S::NV, R = S::R;
   constexpr int SLOTS = S::SLOTS, SPL = S::SPL;
 
-  __shared__ float s_sc[kMaxWaves][SLOTS];
-  __shared__ float s_alpha[kMaxWaves][G];
-  __shared__ float s_m[kMaxWaves][G];
-  __shared__ float s_l[kMaxWaves][G];
-  __shared__ float s_acc[kMaxWaves][G * D];
-  __shared__ int32_t s_tbl[kMaxWaves][64];
-
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
+
+  // per-wavefront LDS, sized by the launch (decode_lds_bytes)
+  extern __shared__ float smem[];
+  float* s_wave = smem + w * S::LDS_FLOATS;
+  float* sc = s_wave;                              // [SLOTS] logits / probabilities
+  float* s_alpha = sc + SLOTS;                     // [G] rescale of this chunk
+  int32_t* tbl = reinterpret_cast<int32_t*>(s_alpha + G);  // [64] block-table window
+  float* s_ml = s_alpha + G + 64;                  // [2G] final max and sum
+  float* s_acc = s_ml + 2 * G;                     // [G*D] final accumulators
+  Unit u;
+  if (!decode_unit<DT, D, G>(p, u)) return;
   const int Hkv = p.num_kv_heads;
   const int Hq = p.num_heads;
-  const int id = blockIdx.x;
-  const int g = id % Hkv;
-  const int rest = id / Hkv;
-  const int part = rest / p.num_seqs;
-  // workgroups are dispatched in index order: taking sequences longest
-  // first leaves the short ones to fill in at the end
-  const int b = ((const __attribute__((address_space(4))) int32_t*)p.order)[rest % p.num_seqs];
-
-  int L = p.context_lens[b];
-  L = min(L, p.max_context_len);
-  if (L <= 0) {
-    if (part == 0) {
-      for (int i = threadIdx.x; i < G * D; i += blockDim.x)
-        store_elem<DT>(p.out, ((size_t)b * Hq + (size_t)g * G) * D + i, 0.0f);
-    }
-    return;
-  }
-  const int P = p.part;
-  const int start = p.window > 0 ? max(0, L - p.window) : 0;
-  const int lo = max(start, part * P);
-  const int hi = min(L, part * P + P);
-  if (lo >= hi) return;
-  const bool single = (start / P) == ((L - 1) / P);
+  const int b = u.b, g = u.g, lo = u.lo, hi = u.hi;
 
   const int e0 = (lane % LPR) * EPL;  // first element of this lane's fragment
   const int rsub = lane / LPR;        // row of this lane within a load
@@ -152,7 +204,6 @@ __global__ __launch_bounds__(256, PA_DECODE_MIN_WAVES) void decode_kernel(Decode
   const int32_t* bt = p.block_tables + (size_t)b * p.max_blocks_per_seq;
   const int log2_bs = p.log2_bs;
   const int last_pg = (hi - 1) >> log2_bs;
-  int32_t* tbl = s_tbl[w];
   int pg0 = -(1 << 30);
   auto refill = [&](int first) {
     pg0 = first;
@@ -244,7 +295,6 @@ __global__ __launch_bounds__(256, PA_DECODE_MIN_WAVES) void decode_kernel(Decode
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
 
-  float* sc = s_sc[w];
   uint4 kr[NI], vr[NI];
   Addr ad;
 
@@ -304,16 +354,20 @@ __global__ __launch_bounds__(256, PA_DECODE_MIN_WAVES) void decode_kernel(Decode
     TransposeReduce<NV, LPR / 2, NV>::run(dots, lane);
     const int jb = tr_base<NV, LPR>(lane);
     const int cs = c * NT;
+    if (p.cap_mul > 0.0f) {
+#pragma unroll
+      for (int t = 0; t < R; ++t) dots[t] = p.cap_mul * tanh_def(dots[t] * p.qk_mul);
+    } else {
+#pragma unroll
+      for (int t = 0; t < R; ++t) dots[t] *= p.qk_mul;
+    }
 #pragma unroll
     for (int t = 0; t < R; ++t) {
       const int j = jb + t;
       const int row = (j / G) * RPI + rsub;
       const int h = j % G;
       const int pos = cs + row;
-      float s = dots[t];
-      s = p.cap_mul > 0.0f ? p.cap_mul * tanh_def(s * p.qk_mul) : s * p.qk_mul;
-      s = (pos >= lo && pos < hi) ? s : kNegInf;
-      sc[row * G + h] = s;
+      sc[row * G + h] = (pos >= lo && pos < hi) ? dots[t] : kNegInf;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -342,7 +396,7 @@ __global__ __launch_bounds__(256, PA_DECODE_MIN_WAVES) void decode_kernel(Decode
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    if (lane < G) s_alpha[w][lane] = alpha;
+    if (lane < G) s_alpha[lane] = alpha;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -350,7 +404,7 @@ __global__ __launch_bounds__(256, PA_DECODE_MIN_WAVES) void decode_kernel(Decode
     // P.V
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float a = s_alpha[w][h];
+      const float a = s_alpha[h];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[h][e] *= a;
     }
@@ -384,53 +438,37 @@ __global__ __launch_bounds__(256, PA_DECODE_MIN_WAVES) void decode_kernel(Decode
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[h][e] += shfl_xor_f(acc[h][e], m);
   if (lane < G) {
-    s_m[w][lane] = m_run;
-    s_l[w][lane] = l_run;
+    s_ml[lane] = m_run;
+    s_ml[G + lane] = l_run;
   }
   if (lane < LPR) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s_acc[w][h * D + e0 + e] = acc[h][e];
+      for (int e = 0; e < EPL; ++e) s_acc[h * D + e0 + e] = acc[h][e];
   }
   __syncthreads();
 
-  for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-    const int h = i / D;
-    const int d = i % D;
-    float M = kNegInf;
-    for (int v = 0; v < nw; ++v) M = fmaxf(M, s_m[v][h]);
-    float den = 0.0f, num = 0.0f;
-    for (int v = 0; v < nw; ++v) {
-      const float f = fast_exp2(s_m[v][h] - M);
-      den += f * s_l[v][h];
-      num += f * s_acc[v][h * D + d];
-    }
-    const size_t hq = (size_t)g * G + h;
-    if (single) {
-      store_elem<DT>(p.out, ((size_t)b * Hq + hq) * D + d, num / den);
-    } else {
-      const size_t pi = ((size_t)b * Hq + hq) * p.num_parts + part;
-      p.tmp_out[pi * D + d] = num / den;
-      if (d == 0) {
-        p.max_logits[pi] = M;
-        p.exp_sums[pi] = den;
-      }
-    }
-  }
+  merge_store<DT, D, G>(p, u, smem, S::LDS_FLOATS, SLOTS + G + 64, SLOTS + G + 64 + 2 * G, nw);
 }
 
-// One wavefront per (sequence, query head): merge the partials of sequences
-// that span more than one non-empty partition.
+// One workgroup of four wavefronts per (sequence, query head): merge the
+// partials of sequences that span more than one non-empty partition.  The
+// wavefronts split the partitions (four loads in flight each), lanes split
+// head_dim, and the four partial sums meet in LDS.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
   constexpr int EPL = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
-  if (wid >= p.num_seqs * p.num_heads) return;
-  const int b = wid / p.num_heads;
-  const int hq = wid % p.num_heads;
-  int L = min(p.context_lens[b], p.max_context_len);
+  typedef const __attribute__((address_space(4))) float cfloat;
+  __shared__ float s_red[4];
+  __shared__ float s_o[4][D];
+  __shared__ float s_den[4];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int b = blockIdx.x / p.num_heads;
+  const int hq = blockIdx.x % p.num_heads;
+  const int L = min(p.context_lens[b], p.max_context_len);
   if (L <= 0) return;
   const int P = p.part;
   const int start = p.window > 0 ? max(0, L - p.window) : 0;
@@ -438,31 +476,39 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
   const int p1 = (L - 1) / P;
   if (p0 == p1) return;
   const size_t base = ((size_t)b * p.num_heads + hq) * p.num_parts;
+  cfloat* ml = (cfloat*)(p.max_logits + base);
+  cfloat* es = (cfloat*)(p.exp_sums + base);
 
+  // the largest partition maximum
   float M = kNegInf;
-  for (int q = p0 + lane; q <= p1; q += 64) M = fmaxf(M, p.max_logits[base + q]);
+  for (int q = p0 + t; q <= p1; q += 256) M = fmaxf(M, p.max_logits[base + q]);
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, shfl_xor_f(M, m));
-  float den = 0.0f;
-  for (int q = p0 + lane; q <= p1; q += 64)
-    den += p.exp_sums[base + q] * fast_exp2(p.max_logits[base + q] - M);
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) den += shfl_xor_f(den, m);
+  if (lane == 0) s_red[w] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
 
   float o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.0f;
+  float den = 0.0f;
+  const float* src = p.tmp_out + base * D + lane * EPL;
 #pragma unroll 4
-  for (int q = p0; q <= p1; ++q) {
-    const float wq = p.exp_sums[base + q] * fast_exp2(p.max_logits[base + q] - M);
-    const float* src = p.tmp_out + (base + q) * D + lane * EPL;
+  for (int q = p0 + w; q <= p1; q += 4) {
+    const float wq = es[q] * fast_exp2(ml[q] - M);
+    den += wq;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] = fmaf(wq, src[e], o[e]);
+    for (int e = 0; e < EPL; ++e) o[e] = fmaf(wq, src[(size_t)q * D + e], o[e]);
   }
-  const float inv = 1.0f / den;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e)
-    store_elem<DT>(p.out, ((size_t)b * p.num_heads + hq) * D + lane * EPL + e, o[e] * inv);
+  for (int e = 0; e < EPL; ++e) s_o[w][lane * EPL + e] = o[e];
+  if (lane == 0) s_den[w] = den;
+  __syncthreads();
+  const float inv = 1.0f / (s_den[0] + s_den[1] + s_den[2] + s_den[3]);
+  for (int d = t; d < D; d += 256) {
+    const float v = (s_o[0][d] + s_o[1][d] + s_o[2][d] + s_o[3][d]) * inv;
+    store_elem<DT>(p.out, ((size_t)b * p.num_heads + hq) * D + d, v);
+  }
 }
 
 }  // namespace pa

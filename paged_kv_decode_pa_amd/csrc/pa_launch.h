@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include "pa_kernels.h"
+#include "pa_mfma.h"
 
 namespace pa {
 
@@ -12,14 +13,26 @@ bool launch_decode_f32(int D, int G, bool paged, dim3 grid, dim3 block, hipStrea
 bool launch_decode_f16(int D, int G, bool paged, dim3 grid, dim3 block, hipStream_t s, const DecodeParams& p);
 bool launch_decode_bf16(int D, int G, bool paged, dim3 grid, dim3 block, hipStream_t s, const DecodeParams& p);
 
+// Matrix-core path (f16/bf16, G in {8, 16}, block_size >= 16); returns
+// false when not built for the shape.
+bool launch_decode_mfma_f16(int D, int G, int tiles, int nw, dim3 grid, hipStream_t s,
+                            const DecodeParams& p);
+bool launch_decode_mfma_bf16(int D, int G, int tiles, int nw, dim3 grid, hipStream_t s,
+                             const DecodeParams& p);
+size_t decode_mfma_lds_bytes(int D, int G, int tiles);
+
 }  // namespace pa
 
 // Expands to the body of a launcher for storage type DT.
 #define PA_DECODE_CASE(DT, DV, GV)                                                  \
   case DV * 16 + GV:                                                                \
-    if (paged) decode_kernel<DT, DV, GV, true><<<grid, block, 0, s>>>(p);           \
-    else decode_kernel<DT, DV, GV, false><<<grid, block, 0, s>>>(p);                \
-    return true;
+  {                                                                                 \
+    const size_t lds = (block.x / 64) * sizeof(float) *                             \
+                       DecodeShape<DT, DV, GV>::LDS_FLOATS;                          \
+    if (paged) decode_kernel<DT, DV, GV, true><<<grid, block, lds, s>>>(p);         \
+    else decode_kernel<DT, DV, GV, false><<<grid, block, lds, s>>>(p);              \
+    return true;                                                                    \
+  }
 
 #define PA_DEFINE_DECODE_LAUNCHER(NAME, DT)                                         \
   bool NAME(int D, int G, bool paged, dim3 grid, dim3 block, hipStream_t s,         \
@@ -31,6 +44,28 @@ bool launch_decode_bf16(int D, int G, bool paged, dim3 grid, dim3 block, hipStre
       PA_DECODE_CASE(DT, 128, 4) PA_DECODE_CASE(DT, 128, 8)                         \
       PA_DECODE_CASE(DT, 256, 1) PA_DECODE_CASE(DT, 256, 2)                         \
       PA_DECODE_CASE(DT, 256, 4) PA_DECODE_CASE(DT, 256, 8)                         \
+      default: return false;                                                        \
+    }                                                                               \
+  }
+
+#define PA_MFMA_CASE(DT, DV, GV, TV)                                                \
+  case (DV * 32 + GV) * 4 + TV: {                                                   \
+    const size_t lds = (size_t)nw * sizeof(float) *                                 \
+                       MfmaShape<DT, DV, GV, TV>::LDS_FLOATS;                       \
+    decode_mfma_kernel<DT, DV, GV, TV><<<grid, dim3(64 * nw), lds, s>>>(p);         \
+    return true;                                                                    \
+  }
+
+#define PA_DEFINE_MFMA_LAUNCHER(NAME, DT)                                           \
+  bool NAME(int D, int G, int tiles, int nw, dim3 grid, hipStream_t s,              \
+            const DecodeParams& p) {                                                \
+    switch ((D * 32 + G) * 4 + tiles) {                                             \
+      PA_MFMA_CASE(DT, 64, 8, 1) PA_MFMA_CASE(DT, 64, 8, 2)                         \
+      PA_MFMA_CASE(DT, 128, 8, 1) PA_MFMA_CASE(DT, 128, 8, 2)                       \
+      PA_MFMA_CASE(DT, 256, 8, 1) PA_MFMA_CASE(DT, 256, 8, 2)                       \
+      PA_MFMA_CASE(DT, 64, 16, 1) PA_MFMA_CASE(DT, 64, 16, 2)                       \
+      PA_MFMA_CASE(DT, 128, 16, 1) PA_MFMA_CASE(DT, 128, 16, 2)                     \
+      PA_MFMA_CASE(DT, 256, 16, 1) PA_MFMA_CASE(DT, 256, 16, 2)                     \
       default: return false;                                                        \
     }                                                                               \
   }

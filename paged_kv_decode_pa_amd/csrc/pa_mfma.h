@@ -1,0 +1,344 @@
+// Matrix-core decode kernel for large GQA groups (G = 8 or 16 query heads
+// per KV head, f16/bf16): the group's q.k^T and P.V become dense 16x16
+// tiles, so they run on MFMA instead of the vector ALUs.
+//
+// Per wavefront and chunk of NT = 16*TILES tokens (inside one KV page):
+//   q.k^T   S^T[t][h] = K[t][:] . Q[h][:]   v_mfma_f32_16x16x32 (M = tokens,
+//           N = heads, K = 32 dims per step).  The A operand is a K row slice:
+//           lane (c16, j) holds token c16, dims 32s+8j..+8, a 16-byte load
+//           straight from HBM; B is the query fragment (zero past head G).
+//           The result leaves lane (c16, j) with head c16 at tokens
+//           16t + 4j + i, i < 4.
+//   softmax lane c16 owns query head c16: per-lane max/exp/sum, the group
+//           max needs two xor shuffles (the 4 lanes of a head).
+//   P.V     O^T[d][h] += V^T[d][t] . P^T[t][h]  (M = 16 dims, N = heads,
+//           K = the chunk's tokens).  B = the lane's own probabilities, in
+//           the token order the q.k result left them (any common order of
+//           the K index is valid); A = V transposed, gathered from LDS.
+//   V is copied HBM -> LDS by the buffer unit (direct-to-LDS 16-byte loads,
+//   no registers in between).  Within a row the 16-byte segments are stored
+//   XOR-swizzled by (row/4) mod 4, so the four lane groups of a transposed
+//   read hit distinct LDS banks.
+#pragma once
+
+#include "pa_kernels.h"
+
+namespace pa {
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// 16x16x32 MFMA on 8 16-bit elements per lane (a and b as raw 16 bytes)
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma_k32(const uint4& a, const uint4& b, f32x4_t c) {
+  if constexpr (DT == DT_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// 16x16x16 MFMA on 4 16-bit elements per lane
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma_k16(const uint2& a, const uint2& b, f32x4_t c) {
+  if constexpr (DT == DT_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                 __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                     __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+}
+
+// two floats -> two packed 16-bit values (round to nearest even)
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (DT == DT_F16)
+    return (uint32_t)f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
+  else
+    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <int DT, int D, int G, int TILES>
+struct MfmaShape {
+  static constexpr int NT = 16 * TILES;             // tokens per chunk
+  static constexpr int KS = D / 32;                 // q.k k-steps
+  static constexpr int MT = D / 16;                 // P.V tiles over head_dim
+  static constexpr int VBYTES = NT * D * 2;         // V chunk in LDS
+  static constexpr int VLOADS = VBYTES / 1024;      // 1 KB direct-to-LDS loads
+  // LDS floats per wavefront: V chunk, block-table window, max/sum, acc
+  static constexpr int V_F = VBYTES / 4;
+  static constexpr int TBL = V_F;
+  static constexpr int ML = TBL + 64;
+  static constexpr int ACC = ML + 2 * G;
+  static constexpr int LDS_FLOATS = ACC + G * D;
+  static_assert(G == 8 || G == 16, "MFMA path: 8 or 16 query heads per KV head");
+  static_assert(VBYTES % 1024 == 0, "chunk must fill whole 1 KB LDS loads");
+};
+
+// byte offset of (row r, element d) of a V chunk in LDS
+template <int D>
+__device__ __forceinline__ uint32_t v_lds_off(int r, int d) {
+  const int f = ((r >> 2) & 3) << 1;
+  return (uint32_t)(r * 2 * D + ((((d >> 3) ^ f)) << 4) + ((d & 7) << 1));
+}
+
+template <int DT, int D, int G, int TILES>
+__global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParams p) {
+  using S = MfmaShape<DT, D, G, TILES>;
+  constexpr int NT = S::NT, KS = S::KS, MT = S::MT, VLOADS = S::VLOADS;
+  constexpr int EB = 2;
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  const int c16 = lane & 15;
+  const int j = lane >> 4;
+
+  extern __shared__ float smem[];
+  float* s_wave = smem + w * S::LDS_FLOATS;
+  char* vbuf = reinterpret_cast<char*>(s_wave);
+  int32_t* tbl = reinterpret_cast<int32_t*>(s_wave + S::TBL);
+
+  Unit u;
+  if (!decode_unit<DT, D, G>(p, u)) return;
+  const int Hq = p.num_heads;
+  const int b = u.b, g = u.g, lo = u.lo, hi = u.hi;
+
+  // query fragments (B operand of q.k): head c16, dims 32s + 8j .. +8
+  uint4 qf[KS];
+  {
+    const char* qb = static_cast<const char*>(p.q) +
+                     (((size_t)b * Hq + (size_t)g * G + c16) * D + 8 * j) * EB;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qf[s] = c16 < G ? ld16(qb + (size_t)s * 32 * EB) : make_uint4(0, 0, 0, 0);
+  }
+
+  const int32_t* bt = p.block_tables + (size_t)b * p.max_blocks_per_seq;
+  const int log2_bs = p.log2_bs;
+  const int last_pg = (hi - 1) >> log2_bs;
+  int pg0 = -(1 << 30);
+  auto refill = [&](int first) {
+    pg0 = first;
+    const int pg = first + lane;
+    const int v = pg <= last_pg ? bt[pg] : 0;
+    tbl[lane] = v;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  const uint32_t row_bytes = (uint32_t)(p.num_kv_heads * D * EB);
+  const uint32_t page_bytes = row_bytes << log2_bs;
+  const uint32_t head_bytes = (uint32_t)(g * D * EB);
+  const char* kbase = static_cast<const char*>(p.k_cache);
+  const char* vbase = static_cast<const char*>(p.v_cache);
+  const char* dummy = static_cast<const char*>(p.q) + ((size_t)b * Hq + (size_t)g * G) * D * EB;
+
+  // per-lane constants of the V copy: instruction i moves LDS bytes
+  // [1024 i, 1024 i + 1024); lane l's 16 bytes hold row r, stored segment
+  // sg ^ f(r) of global segment sg
+  int v_row[VLOADS];
+  uint32_t v_seg_bytes[VLOADS];
+#pragma unroll
+  for (int i = 0; i < VLOADS; ++i) {
+    const int o = i * 1024 + lane * 16;
+    const int r = o / (2 * D);
+    const int sg = ((o % (2 * D)) >> 4) ^ (((r >> 2) & 3) << 1);
+    v_row[i] = r;
+    v_seg_bytes[i] = head_bytes + (uint32_t)(sg * 16);
+  }
+
+  struct Addr {
+    rsrc_t kr, vr;
+    uint32_t soff;
+    int rlo, rhi;  // clamp bounds of chunk rows
+  };
+  auto chunk_addr = [&](int c, Addr& a) {
+    const int cs = c * NT;
+    const int cpg = max(cs, lo) >> log2_bs;
+    if (cpg < pg0 || cpg - pg0 >= 64) refill(cpg);
+    int phys = __builtin_amdgcn_readfirstlane(tbl[cpg - pg0]);
+    phys = ((unsigned)phys < (unsigned)p.num_blocks) ? phys : 0;
+    const uint64_t base = (uint64_t)phys * page_bytes;
+    a.kr = make_rsrc(kbase + base, page_bytes);
+    a.vr = make_rsrc(vbase + base, page_bytes);
+    a.soff = (uint32_t)(cs & ((1 << log2_bs) - 1)) * row_bytes;
+    a.rlo = lo - cs;
+    a.rhi = hi - 1 - cs;
+  };
+  auto dummy_addr = [&](Addr& a) {
+    a.kr = make_rsrc(dummy, (uint32_t)(G * D * EB));
+    a.vr = a.kr;
+    a.soff = 0;
+    a.rlo = 0;
+    a.rhi = 0;
+  };
+  // K fragment (tile t, k-step s): token 16t + c16, dims 32s + 8j
+  auto kload = [&](const Addr& a, int t, int s) -> uint4 {
+    const int r = min(max(16 * t + c16, a.rlo), a.rhi);
+    return ld16_buf(a.kr, (uint32_t)r * row_bytes + head_bytes + (uint32_t)((32 * s + 8 * j) * EB),
+                    a.soff);
+  };
+  auto vcopy = [&](const Addr& a) {
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      const int r = min(max(v_row[i], a.rlo), a.rhi);
+      ld16_buf_to_lds(a.vr, vbuf + i * 1024, (uint32_t)r * row_bytes + v_seg_bytes[i], a.soff);
+    }
+  };
+
+  float m_run = kNegInf;  // running max (base 2) of query head c16
+  float l_run = 0.0f;     // this lane's share of its running sum
+  f32x4_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  uint4 kf[TILES][KS];
+  Addr ad;
+  const int c0 = lo / NT;
+  const int c1 = (hi - 1) / NT;
+  int c = c0 + w;
+  if (c <= c1) {
+    chunk_addr(c, ad);
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kf[t][s] = kload(ad, t, s);
+    __builtin_amdgcn_sched_barrier(0);
+    vcopy(ad);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+#pragma clang loop unroll(disable)
+  for (; c <= c1; c += nw) {
+    // S^T = K . Q^T for each 16-token tile
+    f32x4_t sc[TILES];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      sc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) sc[t] = mfma_k32<DT>(kf[t][s], qf[s], sc[t]);
+    }
+    // the next chunk's K goes in flight
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + nw <= c1) chunk_addr(c + nw, ad);
+    else dummy_addr(ad);
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kf[t][s] = kload(ad, t, s);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // online softmax for head c16 over tokens 16t + 4j + i
+    const int cs = c * NT;
+    float pr[TILES][4];
+    float cmax = kNegInf;
+    if (p.cap_mul > 0.0f) {
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[t][i] = p.cap_mul * tanh_def(sc[t][i] * p.qk_mul);
+    } else {
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[t][i] = sc[t][i] * p.qk_mul;
+    }
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pos = cs + 16 * t + 4 * j + i;
+        pr[t][i] = (pos >= lo && pos < hi) ? pr[t][i] : kNegInf;
+        cmax = fmaxf(cmax, pr[t][i]);
+      }
+    cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
+    cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
+    const float m_new = fmaxf(m_run, cmax);
+    const float alpha = fast_exp2(m_run - m_new);
+    float psum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pr[t][i] = fast_exp2(pr[t][i] - m_new);
+        psum += pr[t][i];
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+
+    // P^T fragment: this lane's probabilities in (tile, i) order
+    uint32_t pk[2 * TILES];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      pk[2 * t] = pack2<DT>(pr[t][0], pr[t][1]);
+      pk[2 * t + 1] = pack2<DT>(pr[t][2], pr[t][3]);
+    }
+
+    // O^T += V^T . P^T, V^T gathered from LDS in the same token order.
+    // The chunk's V copy is older than the TILES*KS K loads just issued.
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(TILES * KS));
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int d = 16 * mt + c16;
+      uint32_t vv[2 * TILES];
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2) {
+          const int r0 = 16 * t + 4 * j + 2 * i2;
+          const uint16_t lo16 = *reinterpret_cast<const uint16_t*>(vbuf + v_lds_off<D>(r0, d));
+          const uint16_t hi16 = *reinterpret_cast<const uint16_t*>(vbuf + v_lds_off<D>(r0 + 1, d));
+          vv[2 * t + i2] = (uint32_t)lo16 | ((uint32_t)hi16 << 16);
+        }
+      if constexpr (TILES == 2)
+        acc[mt] = mfma_k32<DT>(make_uint4(vv[0], vv[1], vv[2], vv[3]),
+                               make_uint4(pk[0], pk[1], pk[2], pk[3]), acc[mt]);
+      else
+        acc[mt] = mfma_k16<DT>(make_uint2(vv[0], vv[1]), make_uint2(pk[0], pk[1]), acc[mt]);
+    }
+    // the next chunk's V goes in flight once every lane has read this one
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // (unconditional like the K loads: after the last chunk it copies a few
+    // bytes of q into the dead buffer, which keeps the wait counts exact)
+    __builtin_amdgcn_sched_barrier(0);
+    vcopy(ad);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // drain the trailing loads before the wavefront moves on
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+
+  // ---- epilogue: sums over the head's four lanes, then the LDS merge ----
+  l_run += shfl_xor_f(l_run, 16);
+  l_run += shfl_xor_f(l_run, 32);
+  if (c16 < G) {
+    if (j == 0) {
+      s_wave[S::ML + c16] = m_run;
+      s_wave[S::ML + G + c16] = l_run;
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_wave[S::ACC + c16 * D + 16 * mt + 4 * j + i] = acc[mt][i];
+  }
+  __syncthreads();
+  merge_store<DT, D, G>(p, u, smem, S::LDS_FLOATS, S::ML, S::ACC, nw);
+}
+
+}  // namespace pa

@@ -108,6 +108,45 @@ def test_small_shapes(shape, waves):
 
 
 # --------------------------------------------------------------------------
+# the matrix-core path (groups of 8 or 16 query heads, 16-bit KV, pages of
+# 16+ tokens) against the oracle, and the vector path on the same shapes
+# --------------------------------------------------------------------------
+MFMA_SHAPES = [
+    # dtype, Hq, Hkv, D, bs, softcap, window, P
+    ("f16", 32, 4, 64, 32, 0.0, 0, 512),
+    ("f16", 32, 4, 64, 16, 0.0, 0, 0),
+    ("bf16", 16, 2, 128, 32, 50.0, 0, 64),
+    ("bf16", 8, 1, 256, 16, 30.0, 45, 32),
+    ("f16", 32, 2, 128, 32, 0.0, 0, 96),
+    ("bf16", 64, 4, 64, 64, 50.0, 100, 0),
+    ("f16", 16, 1, 256, 32, 0.0, 0, 0),
+]
+
+
+@pytest.mark.parametrize("shape", MFMA_SHAPES,
+                         ids=[f"{s[0]}-g{s[1]//s[2]}-d{s[3]}-bs{s[4]}-c{s[5]:g}-w{s[6]}-p{s[7]}" for s in MFMA_SHAPES])
+@pytest.mark.parametrize("path", ["mfma", "valu"])
+def test_group_path_shapes(shape, path):
+    import os
+    from gpu_util import say
+    dt, Hq, Hkv, D, bs, cap, W, P = shape
+    G = Hq // Hkv
+    if path == "valu" and G > 8:
+        pytest.skip("the vector path takes groups of up to 8 heads")
+    say(f"group path {path} {shape}")
+    L = [1, 5, 33, 200, 700, 64, 1000]
+    c = make_case(B=len(L), Hq=Hq, Hkv=Hkv, D=D, bs=bs, dtype=dt, context_lens=L,
+                  softcap=cap, window=W, partition_size=P, seed=sum(map(ord, str(shape))) + 7,
+                  extra_table_cols=2)
+    os.environ["PA_DECODE_MFMA"] = "1" if path == "mfma" else "0"
+    try:
+        for waves in (1, 4):
+            check(c, gpu(c, waves=waves))
+    finally:
+        os.environ.pop("PA_DECODE_MFMA", None)
+
+
+# --------------------------------------------------------------------------
 # invariants and edge cases on the GPU
 # --------------------------------------------------------------------------
 def test_single_key_is_exact():
