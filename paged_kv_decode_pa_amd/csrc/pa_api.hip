@@ -116,10 +116,16 @@ int pa_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads, int 
   return part;
 }
 
-// Workspace layout: order [B] int32 (padded to 256 bytes), then, when the
-// keys are split, tmp_out [B,Hq,NP,D] f32, max_logits [B,Hq,NP] f32,
-// exp_sums [B,Hq,NP] f32.
-static size_t order_bytes(int num_seqs) { return ((size_t)num_seqs * 4 + 255) & ~(size_t)255; }
+// Workspace layout, each part padded to 256 bytes: the plan (sequence order
+// [B] int32, item count, items [B*NP] int32 pairs), then, when the keys are
+// split, tmp_out [B,Hq,NP,D] f32, max_logits [B,Hq,NP] f32, exp_sums
+// [B,Hq,NP] f32.
+static size_t pad256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+static size_t plan_bytes(int num_seqs, int max_context_len, int partition_size) {
+  const size_t np = (size_t)num_parts(max_context_len, partition_size);
+  return pad256((size_t)num_seqs * 4) + 256 + pad256((size_t)num_seqs * np * 8);
+}
 
 static size_t partials_bytes(int num_seqs, int num_heads, int head_dim, int max_context_len,
                              int partition_size) {
@@ -133,7 +139,7 @@ static size_t partials_bytes(int num_seqs, int num_heads, int head_dim, int max_
 size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim, int max_context_len,
                                 int partition_size) {
   if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || partition_size < 0) return 0;
-  return order_bytes(num_seqs) +
+  return plan_bytes(num_seqs, max_context_len, partition_size) +
          partials_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size);
 }
 
@@ -168,10 +174,18 @@ int pa_decode(void* out, void* workspace, size_t workspace_bytes, const void* q,
 
   pa::DecodeParams p{};
   p.out = out;
-  p.order = static_cast<const int32_t*>(workspace);
+  char* wsb = static_cast<char*>(workspace);
+  pa::Plan plan;
+  plan.order = reinterpret_cast<int32_t*>(wsb);
+  plan.num_items = reinterpret_cast<int32_t*>(wsb + pad256((size_t)num_seqs * 4));
+  plan.items = reinterpret_cast<int2*>(wsb + pad256((size_t)num_seqs * 4) + 256);
+  p.order = plan.order;
+  p.num_items = plan.num_items;
+  p.items = plan.items;
   if (partials_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size)) {
     const size_t rows = (size_t)num_seqs * num_heads * np;
-    float* ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + order_bytes(num_seqs));
+    float* ws = reinterpret_cast<float*>(wsb + plan_bytes(num_seqs, max_context_len,
+                                                          partition_size));
     p.tmp_out = ws;
     p.max_logits = ws + rows * head_dim;
     p.exp_sums = p.max_logits + rows;
@@ -212,20 +226,29 @@ int pa_decode(void* out, void* workspace, size_t workspace_bytes, const void* q,
   const long blocks = (long)num_seqs * num_kv_heads * np;
   if (blocks > 0x7fffffffL) return PA_EUNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // One workgroup per (sequence, KV head, partition), unless that grid is
+  // more than twice what the chip holds at once and spans many partitions:
+  // workgroups are dispatched at a bounded rate, so a grid of mostly empty
+  // partitions (one long sequence among short ones) would delay the real
+  // work.  Then a smaller grid loops over the plan's list of non-empty
+  // partitions.
+  const long resident = (long)kNumCUs * 16 / nw;
+  const bool loop = blocks > 2 * resident && np >= 8;
+  if (!loop) plan.items = nullptr;
   pa::plan_kernel<<<dim3(1), dim3(1024), 0, s>>>(context_lens, num_seqs, max_context_len, window,
-                                                static_cast<int32_t*>(workspace));
-  const dim3 grid((unsigned)blocks), block(64 * nw);
+                                                p.part, plan);
+  const dim3 grid((unsigned)(loop ? 2 * resident : blocks)), block(64 * nw);
   // chunks of nt tokens stay inside one page when block_size >= nt
   const bool paged = block_size >= nt;
   bool ok = false;
   if (mfma) {
-    ok = dtype == PA_F16 ? pa::launch_decode_mfma_f16(head_dim, G, tiles, nw, grid, s, p)
-                         : pa::launch_decode_mfma_bf16(head_dim, G, tiles, nw, grid, s, p);
+    ok = dtype == PA_F16 ? pa::launch_decode_mfma_f16(head_dim, G, tiles, loop, nw, grid, s, p)
+                         : pa::launch_decode_mfma_bf16(head_dim, G, tiles, loop, nw, grid, s, p);
   } else {
     switch (dtype) {
-      case PA_F32: ok = pa::launch_decode_f32(head_dim, G, paged, grid, block, s, p); break;
-      case PA_F16: ok = pa::launch_decode_f16(head_dim, G, paged, grid, block, s, p); break;
-      case PA_BF16: ok = pa::launch_decode_bf16(head_dim, G, paged, grid, block, s, p); break;
+      case PA_F32: ok = pa::launch_decode_f32(head_dim, G, paged, loop, grid, block, s, p); break;
+      case PA_F16: ok = pa::launch_decode_f16(head_dim, G, paged, loop, grid, block, s, p); break;
+      case PA_BF16: ok = pa::launch_decode_bf16(head_dim, G, paged, loop, grid, block, s, p); break;
     }
   }
   if (!ok) return PA_EUNSUPPORTED;
@@ -248,8 +271,8 @@ int pa_decode_reduce(void* out, const void* workspace, size_t workspace_bytes,
   if (!workspace || workspace_bytes < need) return PA_EWORKSPACE;
   const int np = num_parts(max_context_len, partition_size);
   const size_t rows = (size_t)num_seqs * num_heads * np;
-  const float* ws = reinterpret_cast<const float*>(static_cast<const char*>(workspace) +
-                                                   order_bytes(num_seqs));
+  const float* ws = reinterpret_cast<const float*>(
+      static_cast<const char*>(workspace) + plan_bytes(num_seqs, max_context_len, partition_size));
   pa::ReduceParams p{};
   p.out = out;
   p.tmp_out = ws;

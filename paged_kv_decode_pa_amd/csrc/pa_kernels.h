@@ -31,7 +31,9 @@ constexpr int kMaxWaves = 8;
 
 struct DecodeParams {
   void* out;               // [B, Hq, D]
-  const int32_t* order;    // [B] sequences, longest first (workspace)
+  const int32_t* order;      // [B] sequences, longest first (workspace)
+  const int32_t* num_items;  // looping launches: number of work items
+  const int2* items;         // looping launches: (sequence, partition) list
   float* tmp_out;          // [B, Hq, NP, D]
   float* max_logits;       // [B, Hq, NP], base-2 logits
   float* exp_sums;         // [B, Hq, NP]
@@ -92,19 +94,10 @@ struct Unit {
   bool single;  // the sequence's attended keys fall in this one partition
 };
 
-// Decodes blockIdx into a unit: KV head fastest, then sequences in the
-// plan's longest-first order, then partitions (so a sequence's partitions
-// are spread over the whole dispatch).  Returns false when the workgroup has
-// no keys to attend to; partition 0 of an empty sequence writes its zero
-// output.
+// Fills the unit's key range.  Returns false when it has no keys to attend
+// to; partition 0 of an empty sequence writes its zero output.
 template <int DT, int D, int G>
-__device__ __forceinline__ bool decode_unit(const DecodeParams& p, Unit& u) {
-  typedef const __attribute__((address_space(4))) int32_t cint32;
-  const int id = blockIdx.x;
-  u.g = id % p.num_kv_heads;
-  const int rest = id / p.num_kv_heads;
-  u.part = rest / p.num_seqs;
-  u.b = ((cint32*)p.order)[rest % p.num_seqs];
+__device__ __forceinline__ bool unit_range(const DecodeParams& p, Unit& u) {
   const int L = min(p.context_lens[u.b], p.max_context_len);
   if (L <= 0) {
     if (u.part == 0)
@@ -118,6 +111,51 @@ __device__ __forceinline__ bool decode_unit(const DecodeParams& p, Unit& u) {
   u.hi = min(L, u.part * P + P);
   u.single = (start / P) == ((L - 1) / P);
   return u.lo < u.hi;
+}
+
+// One unit per workgroup: KV head fastest, then sequences in the plan's
+// longest-first order, then partitions (so a sequence's partitions are
+// spread over the whole dispatch).
+template <int DT, int D, int G>
+__device__ __forceinline__ bool grid_unit(const DecodeParams& p, Unit& u) {
+  typedef const __attribute__((address_space(4))) int32_t cint32;
+  const int id = blockIdx.x;
+  u.g = id % p.num_kv_heads;
+  const int rest = id / p.num_kv_heads;
+  u.part = rest / p.num_seqs;
+  u.b = ((cint32*)p.order)[rest % p.num_seqs];
+  return unit_range<DT, D, G>(p, u);
+}
+
+// Unit `it` of a looping launch: KV head fastest over the plan's item list.
+template <int DT, int D, int G>
+__device__ __forceinline__ bool item_unit(const DecodeParams& p, int it, Unit& u) {
+  typedef const __attribute__((address_space(4))) uint64_t cu64;
+  u.g = it % p.num_kv_heads;
+  // an item is (sequence, partition) as two int32, little-endian
+  const uint64_t item = ((cu64*)p.items)[it / p.num_kv_heads];
+  u.b = (int)(uint32_t)item;
+  u.part = (int)(uint32_t)(item >> 32);
+  return unit_range<DT, D, G>(p, u);
+}
+
+// Runs body(unit) for this workgroup's units: its own one, or (LOOP) every
+// gridDim-th unit of the plan's list, so that a launch whose grid would be
+// mostly empty partitions stays small.
+template <int DT, int D, int G, bool LOOP, typename Body>
+__device__ __forceinline__ void for_units(const DecodeParams& p, Body&& body) {
+  if constexpr (LOOP) {
+    typedef const __attribute__((address_space(4))) int32_t cint32;
+    const int n = *(cint32*)p.num_items * p.num_kv_heads;
+    for (int it = blockIdx.x; it < n; it += gridDim.x) {
+      Unit u;
+      if (item_unit<DT, D, G>(p, it, u)) body(u);
+      __syncthreads();  // LDS is reused by the next unit
+    }
+  } else {
+    Unit u;
+    if (grid_unit<DT, D, G>(p, u)) body(u);
+  }
 }
 
 // Merges the wavefronts' running (max, sum, accumulators) and writes the
@@ -161,7 +199,7 @@ __device__ __forceinline__ void merge_store(const DecodeParams& p, const Unit& u
 #ifndef PA_DECODE_MIN_WAVES
 #define PA_DECODE_MIN_WAVES 1
 #endif
-template <int DT, int D, int G, bool PAGED>
+template <int DT, int D, int G, bool PAGED, bool LOOP>
 __global__ __launch_bounds__(64 * kMaxWaves, PA_DECODE_MIN_WAVES) void decode_kernel(DecodeParams p) {
   using S = DecodeShape<DT, D, G>;
   constexpr int EB = S::EB, EPL = S::EPL, LPR = S::LPR, RPI = S::RPI;
@@ -180,8 +218,7 @@ __global__ __launch_bounds__(64 * kMaxWaves, PA_DECODE_MIN_WAVES) void decode_ke
   int32_t* tbl = reinterpret_cast<int32_t*>(s_alpha + G);  // [64] block-table window
   float* s_ml = s_alpha + G + 64;                  // [2G] final max and sum
   float* s_acc = s_ml + 2 * G;                     // [G*D] final accumulators
-  Unit u;
-  if (!decode_unit<DT, D, G>(p, u)) return;
+  for_units<DT, D, G, LOOP>(p, [&](const Unit& u) {
   const int Hkv = p.num_kv_heads;
   const int Hq = p.num_heads;
   const int b = u.b, g = u.g, lo = u.lo, hi = u.hi;
@@ -450,6 +487,7 @@ __global__ __launch_bounds__(64 * kMaxWaves, PA_DECODE_MIN_WAVES) void decode_ke
   __syncthreads();
 
   merge_store<DT, D, G>(p, u, smem, S::LDS_FLOATS, SLOTS + G + 64, SLOTS + G + 64 + 2 * G, nw);
+  });
 }
 
 // One workgroup of four wavefronts per (sequence, query head): merge the

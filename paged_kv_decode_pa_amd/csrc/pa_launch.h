@@ -9,15 +9,15 @@
 namespace pa {
 
 // Each returns false when (head_dim, group) has no instantiation.
-bool launch_decode_f32(int D, int G, bool paged, dim3 grid, dim3 block, hipStream_t s, const DecodeParams& p);
-bool launch_decode_f16(int D, int G, bool paged, dim3 grid, dim3 block, hipStream_t s, const DecodeParams& p);
-bool launch_decode_bf16(int D, int G, bool paged, dim3 grid, dim3 block, hipStream_t s, const DecodeParams& p);
+bool launch_decode_f32(int D, int G, bool paged, bool loop, dim3 grid, dim3 block, hipStream_t s, const DecodeParams& p);
+bool launch_decode_f16(int D, int G, bool paged, bool loop, dim3 grid, dim3 block, hipStream_t s, const DecodeParams& p);
+bool launch_decode_bf16(int D, int G, bool paged, bool loop, dim3 grid, dim3 block, hipStream_t s, const DecodeParams& p);
 
 // Matrix-core path (f16/bf16, G in {8, 16}, block_size >= 16); returns
 // false when not built for the shape.
-bool launch_decode_mfma_f16(int D, int G, int tiles, int nw, dim3 grid, hipStream_t s,
+bool launch_decode_mfma_f16(int D, int G, int tiles, bool loop, int nw, dim3 grid, hipStream_t s,
                             const DecodeParams& p);
-bool launch_decode_mfma_bf16(int D, int G, int tiles, int nw, dim3 grid, hipStream_t s,
+bool launch_decode_mfma_bf16(int D, int G, int tiles, bool loop, int nw, dim3 grid, hipStream_t s,
                              const DecodeParams& p);
 size_t decode_mfma_lds_bytes(int D, int G, int tiles);
 
@@ -29,13 +29,15 @@ size_t decode_mfma_lds_bytes(int D, int G, int tiles);
   {                                                                                 \
     const size_t lds = (block.x / 64) * sizeof(float) *                             \
                        DecodeShape<DT, DV, GV>::LDS_FLOATS;                          \
-    if (paged) decode_kernel<DT, DV, GV, true><<<grid, block, lds, s>>>(p);         \
-    else decode_kernel<DT, DV, GV, false><<<grid, block, lds, s>>>(p);              \
+    if (paged && loop) decode_kernel<DT, DV, GV, true, true><<<grid, block, lds, s>>>(p);   \
+    else if (paged) decode_kernel<DT, DV, GV, true, false><<<grid, block, lds, s>>>(p);     \
+    else if (loop) decode_kernel<DT, DV, GV, false, true><<<grid, block, lds, s>>>(p);      \
+    else decode_kernel<DT, DV, GV, false, false><<<grid, block, lds, s>>>(p);               \
     return true;                                                                    \
   }
 
 #define PA_DEFINE_DECODE_LAUNCHER(NAME, DT)                                         \
-  bool NAME(int D, int G, bool paged, dim3 grid, dim3 block, hipStream_t s,         \
+  bool NAME(int D, int G, bool paged, bool loop, dim3 grid, dim3 block, hipStream_t s, \
             const DecodeParams& p) {                                                \
     switch (D * 16 + G) {                                                           \
       PA_DECODE_CASE(DT, 64, 1) PA_DECODE_CASE(DT, 64, 2)                           \
@@ -52,12 +54,13 @@ size_t decode_mfma_lds_bytes(int D, int G, int tiles);
   case (DV * 32 + GV) * 4 + TV: {                                                   \
     const size_t lds = (size_t)nw * sizeof(float) *                                 \
                        MfmaShape<DT, DV, GV, TV>::LDS_FLOATS;                       \
-    decode_mfma_kernel<DT, DV, GV, TV><<<grid, dim3(64 * nw), lds, s>>>(p);         \
+    if (loop) decode_mfma_kernel<DT, DV, GV, TV, true><<<grid, dim3(64 * nw), lds, s>>>(p);  \
+    else decode_mfma_kernel<DT, DV, GV, TV, false><<<grid, dim3(64 * nw), lds, s>>>(p);     \
     return true;                                                                    \
   }
 
 #define PA_DEFINE_MFMA_LAUNCHER(NAME, DT)                                           \
-  bool NAME(int D, int G, int tiles, int nw, dim3 grid, hipStream_t s,              \
+  bool NAME(int D, int G, int tiles, bool loop, int nw, dim3 grid, hipStream_t s,   \
             const DecodeParams& p) {                                                \
     switch ((D * 32 + G) * 4 + tiles) {                                             \
       PA_MFMA_CASE(DT, 64, 8, 1) PA_MFMA_CASE(DT, 64, 8, 2)                         \

@@ -15,7 +15,8 @@
 //           K = the chunk's tokens).  B = the lane's own probabilities, in
 //           the token order the q.k result left them (any common order of
 //           the K index is valid); A = V transposed, gathered from LDS.
-//   V is copied HBM -> LDS by the buffer unit (direct-to-LDS 16-byte loads,
+//   Two chunks are in flight per wavefront: K in two register slots, V in
+//   two LDS buffers.  V is copied HBM -> LDS by the buffer unit (direct-to-LDS 16-byte loads,
 //   no registers in between).  Within a row the 16-byte segments are stored
 //   XOR-swizzled by (row/4) mod 4, so the four lane groups of a transposed
 //   read hit distinct LDS banks.
@@ -73,8 +74,8 @@ struct MfmaShape {
   static constexpr int MT = D / 16;                 // P.V tiles over head_dim
   static constexpr int VBYTES = NT * D * 2;         // V chunk in LDS
   static constexpr int VLOADS = VBYTES / 1024;      // 1 KB direct-to-LDS loads
-  // LDS floats per wavefront: V chunk, block-table window, max/sum, acc
-  static constexpr int V_F = VBYTES / 4;
+  // LDS floats per wavefront: two V chunks, block-table window, max/sum, acc
+  static constexpr int V_F = 2 * VBYTES / 4;
   static constexpr int TBL = V_F;
   static constexpr int ML = TBL + 64;
   static constexpr int ACC = ML + 2 * G;
@@ -90,7 +91,7 @@ __device__ __forceinline__ uint32_t v_lds_off(int r, int d) {
   return (uint32_t)(r * 2 * D + ((((d >> 3) ^ f)) << 4) + ((d & 7) << 1));
 }
 
-template <int DT, int D, int G, int TILES>
+template <int DT, int D, int G, int TILES, bool LOOP>
 __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParams p) {
   using S = MfmaShape<DT, D, G, TILES>;
   constexpr int NT = S::NT, KS = S::KS, MT = S::MT, VLOADS = S::VLOADS;
@@ -107,8 +108,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
   char* vbuf = reinterpret_cast<char*>(s_wave);
   int32_t* tbl = reinterpret_cast<int32_t*>(s_wave + S::TBL);
 
-  Unit u;
-  if (!decode_unit<DT, D, G>(p, u)) return;
+  for_units<DT, D, G, LOOP>(p, [&](const Unit& u) {
   const int Hq = p.num_heads;
   const int b = u.b, g = u.g, lo = u.lo, hi = u.hi;
 
@@ -188,11 +188,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
     return ld16_buf(a.kr, (uint32_t)r * row_bytes + head_bytes + (uint32_t)((32 * s + 8 * j) * EB),
                     a.soff);
   };
-  auto vcopy = [&](const Addr& a) {
+  auto vcopy = [&](const Addr& a, char* vb) {
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
       const int r = min(max(v_row[i], a.rlo), a.rhi);
-      ld16_buf_to_lds(a.vr, vbuf + i * 1024, (uint32_t)r * row_bytes + v_seg_bytes[i], a.soff);
+      ld16_buf_to_lds(a.vr, vb + i * 1024, (uint32_t)r * row_bytes + v_seg_bytes[i], a.soff);
     }
   };
 
@@ -202,44 +202,41 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  uint4 kf[TILES][KS];
-  Addr ad;
   const int c0 = lo / NT;
   const int c1 = (hi - 1) / NT;
-  int c = c0 + w;
-  if (c <= c1) {
-    chunk_addr(c, ad);
+  constexpr int NK = TILES * KS;  // K loads per chunk
+  constexpr int NV = VLOADS;      // V copies per chunk
+  auto addr_of = [&](int cc, Addr& a) {
+    if (cc <= c1) chunk_addr(cc, a);
+    else dummy_addr(a);
+  };
+  auto issue_k = [&](const Addr& a, uint4 (&k)[TILES][KS]) {
 #pragma unroll
     for (int t = 0; t < TILES; ++t)
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kf[t][s] = kload(ad, t, s);
-    __builtin_amdgcn_sched_barrier(0);
-    vcopy(ad);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+      for (int s = 0; s < KS; ++s) k[t][s] = kload(a, t, s);
+  };
 
-#pragma clang loop unroll(disable)
-  for (; c <= c1; c += nw) {
-    // S^T = K . Q^T for each 16-token tile
+  // One chunk cc: q.k on the K slot, then that slot and V buffer `vb` are
+  // refilled with chunk cn (a few bytes of q past the last chunk), so two
+  // chunks stay in flight while this one is computed.  A chunk past the end
+  // is fully masked and leaves the running state unchanged.
+  auto step = [&](int cc, int cn, uint4 (&k)[TILES][KS], char* vb) {
     f32x4_t sc[TILES];
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
       sc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) sc[t] = mfma_k32<DT>(kf[t][s], qf[s], sc[t]);
+      for (int s = 0; s < KS; ++s) sc[t] = mfma_k32<DT>(k[t][s], qf[s], sc[t]);
     }
-    // the next chunk's K goes in flight
     __builtin_amdgcn_sched_barrier(0);
-    if (c + nw <= c1) chunk_addr(c + nw, ad);
-    else dummy_addr(ad);
-#pragma unroll
-    for (int t = 0; t < TILES; ++t)
-#pragma unroll
-      for (int s = 0; s < KS; ++s) kf[t][s] = kload(ad, t, s);
+    Addr an;
+    addr_of(cn, an);
+    issue_k(an, k);
     __builtin_amdgcn_sched_barrier(0);
 
     // online softmax for head c16 over tokens 16t + 4j + i
-    const int cs = c * NT;
+    const int cs = cc * NT;
     float pr[TILES][4];
     float cmax = kNegInf;
     if (p.cap_mul > 0.0f) {
@@ -287,8 +284,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
     }
 
     // O^T += V^T . P^T, V^T gathered from LDS in the same token order.
-    // The chunk's V copy is older than the TILES*KS K loads just issued.
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(TILES * KS));
+    // Issued after this chunk's V copy: the other slot's K and V, and the K
+    // just issued.
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * NK + NV));
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -299,8 +297,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
 #pragma unroll
         for (int i2 = 0; i2 < 2; ++i2) {
           const int r0 = 16 * t + 4 * j + 2 * i2;
-          const uint16_t lo16 = *reinterpret_cast<const uint16_t*>(vbuf + v_lds_off<D>(r0, d));
-          const uint16_t hi16 = *reinterpret_cast<const uint16_t*>(vbuf + v_lds_off<D>(r0 + 1, d));
+          const uint16_t lo16 = *reinterpret_cast<const uint16_t*>(vb + v_lds_off<D>(r0, d));
+          const uint16_t hi16 = *reinterpret_cast<const uint16_t*>(vb + v_lds_off<D>(r0 + 1, d));
           vv[2 * t + i2] = (uint32_t)lo16 | ((uint32_t)hi16 << 16);
         }
       if constexpr (TILES == 2)
@@ -309,15 +307,36 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
       else
         acc[mt] = mfma_k16<DT>(make_uint2(vv[0], vv[1]), make_uint2(pk[0], pk[1]), acc[mt]);
     }
-    // the next chunk's V goes in flight once every lane has read this one
+    // refill the buffer once every lane has read it
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // (unconditional like the K loads: after the last chunk it copies a few
-    // bytes of q into the dead buffer, which keeps the wait counts exact)
     __builtin_amdgcn_sched_barrier(0);
-    vcopy(ad);
+    vcopy(an, vb);
     __builtin_amdgcn_sched_barrier(0);
+  };
+
+  uint4 kf0[TILES][KS], kf1[TILES][KS];
+  char* vb0 = vbuf;
+  char* vb1 = vbuf + S::VBYTES;
+  int c = c0 + w;
+  if (c <= c1) {
+    Addr a;
+    addr_of(c, a);
+    issue_k(a, kf0);
+    __builtin_amdgcn_sched_barrier(0);
+    vcopy(a, vb0);
+    __builtin_amdgcn_sched_barrier(0);
+    addr_of(c + nw, a);
+    issue_k(a, kf1);
+    __builtin_amdgcn_sched_barrier(0);
+    vcopy(a, vb1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma clang loop unroll(disable)
+    for (; c <= c1; c += 2 * nw) {
+      step(c, c + 2 * nw, kf0, vb0);
+      step(c + nw, c + 3 * nw, kf1, vb1);
+    }
   }
   // drain the trailing loads before the wavefront moves on
   __builtin_amdgcn_s_waitcnt(0);
@@ -339,6 +358,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
   }
   __syncthreads();
   merge_store<DT, D, G>(p, u, smem, S::LDS_FLOATS, S::ML, S::ACC, nw);
+  });
 }
 
 }  // namespace pa

@@ -1,27 +1,66 @@
-// Work ordering for pa_decode.
+// Work plan for pa_decode: one workgroup sorts the sequences by attended
+// length, longest first, and (for launches that loop over work) lists every
+// (sequence, partition) that holds keys, so no workgroup is spent on
+// partitions past a sequence's end.
 #pragma once
 
 #include "pa_device.h"
 
 namespace pa {
 
-// One workgroup: order the sequences by attended length, longest first
-// (counting sort over 256 length buckets; order within a bucket is
-// arbitrary, which no result depends on).
+struct Plan {
+  int32_t* order;      // [B] sequences, longest first
+  int32_t* num_items;  // [1] number of items
+  int2* items;         // [<= B * NP] (sequence, partition); null: not listed
+};
+
+// Exclusive prefix sum over the workgroup; *total gets the sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* s_tmp, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) s_tmp[w] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int k = 0; k < (int)(blockDim.x >> 6); ++k) {
+      const int t = s_tmp[k];
+      s_tmp[k] = run;
+      run += t;
+    }
+    s_tmp[16] = run;
+  }
+  __syncthreads();
+  const int r = x - v + s_tmp[w];
+  *total = s_tmp[16];
+  __syncthreads();
+  return r;
+}
+
+// part: partition size in tokens (max_context_len when keys are not split)
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ context_lens,
                                                     int num_seqs, int max_context_len, int window,
-                                                    int32_t* __restrict__ order) {
+                                                    int part, Plan plan) {
   constexpr int NBK = 256;
   __shared__ int hist[NBK];
   __shared__ int offs[NBK];
+  __shared__ int s_tmp[17];
   const int t = threadIdx.x;
   if (t < NBK) hist[t] = 0;
   __syncthreads();
   const int span = max(max_context_len, 1);
+  auto length = [&](int b) { return min(max(context_lens[b], 0), max_context_len); };
+  // counting sort over 256 length buckets, descending: the longest
+  // sequences land in bucket 0 (order within a bucket is arbitrary, which
+  // no result depends on)
   auto bucket = [&](int b) {
-    int n = min(max(context_lens[b], 0), max_context_len);
+    int n = length(b);
     if (window > 0) n = min(n, window);
-    // descending: the longest sequences land in bucket 0
     return NBK - 1 - (int)(((long long)n * (NBK - 1)) / span);
   };
   for (int b = t; b < num_seqs; b += blockDim.x) atomicAdd(&hist[bucket(b)], 1);
@@ -34,7 +73,33 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     }
   }
   __syncthreads();
-  for (int b = t; b < num_seqs; b += blockDim.x) order[atomicAdd(&offs[bucket(b)], 1)] = b;
+  for (int b = t; b < num_seqs; b += blockDim.x) plan.order[atomicAdd(&offs[bucket(b)], 1)] = b;
+  if (plan.items == nullptr) return;
+  __syncthreads();
+
+  // the non-empty partitions of each sequence, sequences in plan order; an
+  // empty sequence keeps one item (its partition 0 writes the zero output)
+  int base = 0;
+  for (int k0 = 0; k0 < num_seqs; k0 += blockDim.x) {
+    const int k = k0 + t;
+    int b = 0, first = 0, n = 0;
+    if (k < num_seqs) {
+      b = plan.order[k];
+      const int L = length(b);
+      if (L <= 0) {
+        n = 1;
+      } else {
+        const int start = window > 0 ? max(0, L - window) : 0;
+        first = start / part;
+        n = (L - 1) / part - first + 1;
+      }
+    }
+    int total;
+    const int off = base + block_exclusive_scan(n, s_tmp, &total);
+    for (int i = 0; i < n; ++i) plan.items[off + i] = make_int2(b, first + i);
+    base += total;
+  }
+  if (t == 0) *plan.num_items = base;
 }
 
 }  // namespace pa

@@ -36,15 +36,19 @@ def test_status_strings():
 
 
 def test_workspace_size_arithmetic():
-    # order [B] int32 padded to 256 B, then [B, Hq, NP, D] fp32 + two [B, Hq, NP] fp32
-    def order(B):
-        return (B * 4 + 255) // 256 * 256
+    # plan: order [B] int32, a 256-byte item count, items [B * NP] int32
+    # pairs (each padded to 256 B); then [B, Hq, NP, D] fp32 + two [B, Hq, NP] fp32
+    def pad(n):
+        return (n + 255) // 256 * 256
+
+    def plan(B, NP):
+        return pad(B * 4) + 256 + pad(B * NP * 8)
     B, Hq, D, L, P = 33, 32, 64, 131072, 512
     NP = L // P
-    assert pa.workspace_size(B, Hq, D, L, P) == order(B) + B * Hq * NP * (D + 2) * 4
-    assert pa.workspace_size(B, Hq, D, L, 0) == order(B)          # no split
-    assert pa.workspace_size(B, Hq, D, 300, 512) == order(B)      # one partition
-    assert pa.workspace_size(4, 8, 256, 513, 512) == 256 + 4 * 8 * 2 * 258 * 4
+    assert pa.workspace_size(B, Hq, D, L, P) == plan(B, NP) + B * Hq * NP * (D + 2) * 4
+    assert pa.workspace_size(B, Hq, D, L, 0) == plan(B, 1)         # no split
+    assert pa.workspace_size(B, Hq, D, 300, 512) == plan(B, 1)     # one partition
+    assert pa.workspace_size(4, 8, 256, 513, 512) == plan(4, 2) + 4 * 8 * 2 * 258 * 4
     assert pa.workspace_size(0, 8, 256, 513, 512) == 0
 
 

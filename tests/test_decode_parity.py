@@ -146,6 +146,25 @@ def test_group_path_shapes(shape, path):
         os.environ.pop("PA_DECODE_MFMA", None)
 
 
+def test_looping_launch_over_many_partitions():
+    """One long sequence among short ones with small partitions: the grid of
+    every (sequence, KV head, partition) would be mostly empty, so the launch
+    loops over the plan's list of non-empty partitions instead."""
+    import paged_kv_decode_pa_amd as pa
+    from gpu_util import say
+    say("looping launch")
+    rng = np.random.default_rng(12)
+    L = [8192] + list(rng.integers(1, 300, size=39))
+    c = make_case(B=40, Hq=8, Hkv=4, D=128, bs=16, dtype="bf16", context_lens=L,
+                  softcap=50.0, partition_size=64, seed=13)
+    NP = -(-8192 // 64)
+    assert 40 * 4 * NP > 2 * 256 * 16  # more workgroups than the heuristic allows
+    check(c, gpu(c))
+    c5 = make_case(B=40, Hq=32, Hkv=4, D=64, bs=32, dtype="f16", context_lens=L,
+                   partition_size=64, seed=14)
+    check(c5, gpu(c5))
+
+
 # --------------------------------------------------------------------------
 # invariants and edge cases on the GPU
 # --------------------------------------------------------------------------
