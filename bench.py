@@ -119,6 +119,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--no-check", action="store_true", help="skip the parity spot-check")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay of the step")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -194,6 +196,30 @@ def main():
     decode_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
     print(f"[bench] timed {args.steps} steps: {ms_step*1e3:.1f} us/step wall, "
           f"pa_decode {decode_ms*1e3:.1f} us (HIP events)", file=sys.stderr, flush=True)
+
+    # the same step captured once into a HIP graph and replayed K times
+    graph = None
+    if not args.no_graph:
+        gstream = torch.cuda.Stream()
+        st = pa.Step(q, kc, vc, bt, cl, case.scale, case.softcap, case.window,
+                     partition_size=P, max_context_len=maxL, out=out, key=key, value=value,
+                     slot_mapping=slots)
+        st.capture(gstream)
+        with torch.cuda.stream(gstream):
+            for _ in range(args.warmup):
+                st.replay(gstream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(gstream):
+            for _ in range(args.steps):
+                st.replay(gstream)
+        torch.cuda.synchronize()
+        g_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        st.close()
+        graph = {"ms_per_step": round(g_ms, 5),
+                 "value": round(case.algorithmic_bytes()["total"] / (g_ms / 1e3) / 1e9, 2),
+                 "unit": "GB/s"}
+        print(f"[bench] graph replay: {g_ms*1e3:.1f} us/step", file=sys.stderr, flush=True)
 
     if args.calib_copy_mib:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -273,6 +299,7 @@ def main():
             "algorithmic_bytes_per_launch": ab["decode"],
             "kernel_sources": digest,
         },
+        "graph_replay": graph,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -143,6 +143,66 @@ int pa_decode_reduce(void* out, const void* workspace, size_t workspace_bytes,
                      int partition_size, int window, pa_dtype dtype,
                      void* stream);
 
+/*
+ * One layer-step: pa_reshape_and_cache (when num_tokens > 0), pa_decode and
+ * pa_decode_reduce with the arguments below, on one stream.  The step can
+ * also be captured once into a HIP graph and replayed: static graph execution
+ * removes the per-launch host cost where it dominates (small batches, short
+ * contexts) — the pages list pre-compiled execution plans among the engines'
+ * techniques (GeeeekExplorer/nano-vllm on awesome-repositories, "Features":
+ * graph compilation, static graph execution).  A replay reads and writes the
+ * same buffers as the capture; their contents may change between replays,
+ * their addresses and the host-side sizes may not.
+ */
+typedef struct {
+  /* reshape_and_cache (skipped when num_tokens == 0) */
+  const void* key;
+  const void* value;
+  const int64_t* slot_mapping;
+  int num_tokens;
+  /* decode */
+  void* out;
+  void* workspace;
+  size_t workspace_bytes;
+  const void* q;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  const int32_t* context_lens;
+  int max_context_len;
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int head_dim;
+  int block_size;
+  int num_blocks;
+  float scale;
+  float softcap;
+  int window;
+  int partition_size;
+  pa_dtype dtype;
+} pa_step_args;
+
+/* Runs the step on `stream` (no graph).  Returns the first failing status. */
+int pa_step(const pa_step_args* args, void* stream);
+
+typedef struct pa_step_graph pa_step_graph; /* opaque */
+
+/*
+ * Captures the step on `stream` (which must not be capturing already) into a
+ * graph and instantiates it.  Set-up call: it allocates host-side graph
+ * objects, nothing on the device; free them with pa_step_graph_destroy.
+ * Nothing is executed during capture.  *graph is set only on success.
+ */
+int pa_step_graph_create(const pa_step_args* args, void* stream, pa_step_graph** graph);
+
+/* Enqueues one replay of the captured step on `stream`. */
+int pa_step_graph_launch(pa_step_graph* graph, void* stream);
+
+/* Frees the graph (NULL is a no-op). */
+int pa_step_graph_destroy(pa_step_graph* graph);
+
 #ifdef __cplusplus
 }
 #endif

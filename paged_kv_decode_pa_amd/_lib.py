@@ -18,7 +18,26 @@ STATUS = {0: "PA_OK", -1: "PA_EINVAL", -2: "PA_EUNSUPPORTED", -3: "PA_EWORKSPACE
 
 # every symbol include/pa.h declares
 EXPORTS = ("pa_status_string", "pa_reshape_and_cache", "pa_decode_partition_size",
-           "pa_decode_workspace_size", "pa_decode", "pa_decode_reduce")
+           "pa_decode_workspace_size", "pa_decode", "pa_decode_reduce", "pa_step",
+           "pa_step_graph_create", "pa_step_graph_launch", "pa_step_graph_destroy")
+
+
+class StepArgs(ctypes.Structure):
+    """pa_step_args (include/pa.h)."""
+    _fields_ = [
+        ("key", ctypes.c_void_p), ("value", ctypes.c_void_p),
+        ("slot_mapping", ctypes.c_void_p), ("num_tokens", ctypes.c_int),
+        ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t), ("q", ctypes.c_void_p),
+        ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("block_tables", ctypes.c_void_p), ("max_blocks_per_seq", ctypes.c_int),
+        ("context_lens", ctypes.c_void_p), ("max_context_len", ctypes.c_int),
+        ("num_seqs", ctypes.c_int), ("num_heads", ctypes.c_int),
+        ("num_kv_heads", ctypes.c_int), ("head_dim", ctypes.c_int),
+        ("block_size", ctypes.c_int), ("num_blocks", ctypes.c_int),
+        ("scale", ctypes.c_float), ("softcap", ctypes.c_float), ("window", ctypes.c_int),
+        ("partition_size", ctypes.c_int), ("dtype", ctypes.c_int),
+    ]
 
 _lib = None
 
@@ -52,6 +71,15 @@ def load() -> ctypes.CDLL:
                               i32, i32, i32, i32, i32, i32, f32, f32, i32, i32, i32, vp]
     lib.pa_decode_reduce.restype = i32
     lib.pa_decode_reduce.argtypes = [vp, vp, sz, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+    sp = ctypes.POINTER(StepArgs)
+    lib.pa_step.restype = i32
+    lib.pa_step.argtypes = [sp, vp]
+    lib.pa_step_graph_create.restype = i32
+    lib.pa_step_graph_create.argtypes = [sp, vp, ctypes.POINTER(ctypes.c_void_p)]
+    lib.pa_step_graph_launch.restype = i32
+    lib.pa_step_graph_launch.argtypes = [vp, vp]
+    lib.pa_step_graph_destroy.restype = i32
+    lib.pa_step_graph_destroy.argtypes = [vp]
     _lib = lib
     return lib
 

@@ -1,0 +1,77 @@
+// The layer step (reshape_and_cache + decode + reduce) as one call, and its
+// capture into a HIP graph for replay.
+#include <new>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/pa.h"
+
+struct pa_step_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+extern "C" {
+
+int pa_step(const pa_step_args* a, void* stream) {
+  if (!a) return PA_EINVAL;
+  int st = PA_OK;
+  if (a->num_tokens > 0) {
+    st = pa_reshape_and_cache(a->key, a->value, a->k_cache, a->v_cache, a->slot_mapping,
+                              a->num_tokens, a->num_blocks, a->block_size, a->num_kv_heads,
+                              a->head_dim, a->dtype, stream);
+    if (st != PA_OK) return st;
+  }
+  st = pa_decode(a->out, a->workspace, a->workspace_bytes, a->q, a->k_cache, a->v_cache,
+                 a->block_tables, a->max_blocks_per_seq, a->context_lens, a->max_context_len,
+                 a->num_seqs, a->num_heads, a->num_kv_heads, a->head_dim, a->block_size,
+                 a->num_blocks, a->scale, a->softcap, a->window, a->partition_size, a->dtype,
+                 stream);
+  if (st != PA_OK) return st;
+  return pa_decode_reduce(a->out, a->workspace, a->workspace_bytes, a->context_lens,
+                          a->max_context_len, a->num_seqs, a->num_heads, a->head_dim,
+                          a->partition_size, a->window, a->dtype, stream);
+}
+
+int pa_step_graph_create(const pa_step_args* a, void* stream, pa_step_graph** out) {
+  if (!a || !out || !stream) return PA_EINVAL;  // capture needs a created stream
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) != hipSuccess)
+    return PA_ELAUNCH;
+  const int st = pa_step(a, stream);
+  hipGraph_t graph = nullptr;
+  const hipError_t end = hipStreamEndCapture(s, &graph);
+  if (st != PA_OK || end != hipSuccess || !graph) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return st != PA_OK ? st : PA_ELAUNCH;
+  }
+  hipGraphExec_t exec = nullptr;
+  if (hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    return PA_ELAUNCH;
+  }
+  pa_step_graph* g = new (std::nothrow) pa_step_graph{graph, exec};
+  if (!g) {
+    (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(graph);
+    return PA_ELAUNCH;
+  }
+  *out = g;
+  return PA_OK;
+}
+
+int pa_step_graph_launch(pa_step_graph* g, void* stream) {
+  if (!g) return PA_EINVAL;
+  return hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK
+                                                                                 : PA_ELAUNCH;
+}
+
+int pa_step_graph_destroy(pa_step_graph* g) {
+  if (!g) return PA_OK;
+  (void)hipGraphExecDestroy(g->exec);
+  (void)hipGraphDestroy(g->graph);
+  delete g;
+  return PA_OK;
+}
+
+}  // extern "C"

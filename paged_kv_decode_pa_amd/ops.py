@@ -5,6 +5,7 @@ HIP stream.  All arithmetic runs in the library's kernels.
 """
 from __future__ import annotations
 
+import ctypes
 from typing import Optional
 
 import torch
@@ -146,3 +147,79 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, softcap=0.0, 
                       max_context_len, scale, softcap, window, partition_size)
     decode_reduce(out, workspace, context_lens, max_context_len, partition_size, window)
     return out
+
+
+class Step:
+    """One layer-step over fixed buffers: reshape_and_cache of the new rows
+    (if given), pa_decode and pa_decode_reduce, run through pa_step, or
+    captured once into a HIP graph (``capture``) and replayed with
+    ``replay``.  Buffer contents may change between runs; the tensors (and
+    so their addresses) and the host-side sizes are fixed at construction."""
+
+    def __init__(self, q, k_cache, v_cache, block_tables, context_lens, scale, softcap=0.0,
+                 window=0, partition_size=None, max_context_len=None, out=None,
+                 key=None, value=None, slot_mapping=None):
+        B, Hq, D, NB, bs, Hkv = _shapes(q, k_cache, block_tables)
+        _dev(q, k_cache, v_cache, block_tables, context_lens, key, value, slot_mapping)
+        if max_context_len is None:
+            max_context_len = int(context_lens.max().item()) if B else 0
+        if partition_size is None:
+            partition_size = globals()["partition_size"](B, Hq, Hkv, D, bs, max_context_len,
+                                                         window, q.dtype)
+        self.out = torch.empty_like(q) if out is None else out
+        self.workspace = alloc_workspace(B, Hq, D, max_context_len, partition_size, q.device)
+        # keep every buffer alive as long as the step (and its graph) exists
+        self._keep = (q, k_cache, v_cache, block_tables, context_lens, key, value,
+                      slot_mapping, self.out, self.workspace)
+        a = _lib.StepArgs()
+        if slot_mapping is not None:
+            a.key, a.value, a.slot_mapping = key.data_ptr(), value.data_ptr(), slot_mapping.data_ptr()
+            a.num_tokens = slot_mapping.shape[0]
+        a.out, a.q = self.out.data_ptr(), q.data_ptr()
+        a.workspace = self.workspace.data_ptr() if self.workspace is not None else None
+        a.workspace_bytes = (self.workspace.numel() * 4) if self.workspace is not None else 0
+        a.k_cache, a.v_cache = k_cache.data_ptr(), v_cache.data_ptr()
+        a.block_tables, a.max_blocks_per_seq = block_tables.data_ptr(), block_tables.shape[1]
+        a.context_lens, a.max_context_len = context_lens.data_ptr(), int(max_context_len)
+        a.num_seqs, a.num_heads, a.num_kv_heads, a.head_dim = B, Hq, Hkv, D
+        a.block_size, a.num_blocks = bs, NB
+        a.scale, a.softcap, a.window = float(scale), float(softcap), int(window)
+        a.partition_size, a.dtype = int(partition_size), _dt(q)
+        self.args = a
+        self.partition_size = int(partition_size)
+        self._graph = None
+
+    def run(self):
+        """Enqueue the step on torch's current stream."""
+        _lib.check("pa_step", _lib.load().pa_step(ctypes.byref(self.args), _stream()))
+        return self.out
+
+    def capture(self, stream):
+        """Capture the step on ``stream`` (a torch.cuda.Stream, not the
+        default stream) into a HIP graph."""
+        self.close()
+        h = ctypes.c_void_p()
+        _lib.check("pa_step_graph_create", _lib.load().pa_step_graph_create(
+            ctypes.byref(self.args), stream.cuda_stream, ctypes.byref(h)))
+        self._graph = h
+        return self
+
+    def replay(self, stream=None):
+        """Enqueue one replay of the captured step (on ``stream`` or torch's
+        current stream)."""
+        if self._graph is None:
+            raise RuntimeError("capture() first")
+        s = (stream or torch.cuda.current_stream()).cuda_stream
+        _lib.check("pa_step_graph_launch", _lib.load().pa_step_graph_launch(self._graph, s))
+        return self.out
+
+    def close(self):
+        if self._graph is not None:
+            _lib.load().pa_step_graph_destroy(self._graph)
+            self._graph = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

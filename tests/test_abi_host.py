@@ -135,3 +135,38 @@ def test_binding_refuses_host_tensors():
         pa.decode(q, torch.zeros(4, 16, 1, 64), torch.zeros(4, 16, 1, 64),
                   torch.zeros(1, 1, dtype=torch.int32), torch.ones(1, dtype=torch.int32),
                   0.125, max_context_len=1, partition_size=0)
+
+
+def test_step_args_layout_matches_the_header(tmp_path):
+    """The ctypes mirror of pa_step_args has the C struct's size and offsets
+    (checked with the host C compiler)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    fields = [f for f, _ in _lib.StepArgs._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text(
+        "#include <stdio.h>\n#include <stddef.h>\n#include \"pa.h\"\n"
+        "int main(void) { printf(\"%zu\\n\", sizeof(pa_step_args));\n"
+        + "".join(f'  printf("%zu\\n", offsetof(pa_step_args, {f}));\n' for f in fields)
+        + "  return 0; }\n")
+    exe = tmp_path / "layout"
+    # pa.h only needs the standard headers for this; hipStream_t is void*
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(_lib.StepArgs)
+    for f, off in zip(fields, got[1:]):
+        assert getattr(_lib.StepArgs, f).offset == off, f
+
+
+def test_step_graph_argument_checks():
+    lib = _lib.load()
+    assert lib.pa_step(None, None) == -1
+    h = ctypes.c_void_p()
+    assert lib.pa_step_graph_create(None, None, ctypes.byref(h)) == -1
+    assert lib.pa_step_graph_launch(None, None) == -1
+    assert lib.pa_step_graph_destroy(None) == 0
