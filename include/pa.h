@@ -82,6 +82,24 @@ int pa_reshape_and_cache(const void* key, const void* value,
                          int head_dim, pa_dtype dtype, void* stream);
 
 /*
+ * Copy whole KV blocks (every slot, every KV head, K and V):
+ *   k_cache[dst] = k_cache[src], v_cache[dst] = v_cache[src]
+ * for each pair (src, dst) = (block_mapping[2i], block_mapping[2i+1]),
+ * i < num_pairs.  This is the copy-on-write step of block sharing: sequences
+ * with a common prefix point their block tables at the same physical blocks
+ * (ovshake/nano-vllm README, "Features": prefix caching shares KV blocks of
+ * common prefixes; GeeeekExplorer/nano-vllm, "Features": non-contiguous
+ * blocks enable sharing), and a sequence about to write into a shared,
+ * partly filled block first gets a private copy.  Bit-exact.  Pairs with an
+ * id outside [0, num_blocks) are skipped.  Caller contract: no block is the
+ * destination of two pairs or both a source and a destination.
+ *   block_mapping  [num_pairs, 2] int64, device memory
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int num_pairs,
+                   int num_blocks, int block_size, int num_kv_heads, int head_dim,
+                   pa_dtype dtype, void* stream);
+
+/*
  * The partition size the library would pick for this shape (tokens per
  * split-K partition; 0 means one partition per sequence).  Host-only.
  */

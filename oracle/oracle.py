@@ -68,6 +68,20 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping):
     return kc, vc
 
 
+def copy_blocks(k_cache, v_cache, block_mapping):
+    """Return copies of the caches with whole block dst replaced by block src
+    for each (src, dst) pair (the copy-on-write of a shared block); pairs with
+    an id outside the pool are skipped.  Bit copies."""
+    kc = k_cache.copy()
+    vc = v_cache.copy()
+    NB = kc.shape[0]
+    for src, dst in np.asarray(block_mapping, dtype=np.int64).reshape(-1, 2):
+        if 0 <= src < NB and 0 <= dst < NB:
+            kc[dst] = k_cache[src]
+            vc[dst] = v_cache[src]
+    return kc, vc
+
+
 # --------------------------------------------------------------------------
 # decode attention
 # --------------------------------------------------------------------------

@@ -5,9 +5,10 @@ package is a thin binding that marshals torch tensors (device memory) and
 torch's current stream into those calls.
 """
 from ._lib import EXPORTS, LIB_PATH, PaError, load, status_string
-from .ops import (Step, alloc_workspace, decode, decode_partitions, decode_reduce,
+from .ops import (Step, alloc_workspace, copy_blocks, decode, decode_partitions, decode_reduce,
                   partition_size, reshape_and_cache, workspace_size)
 
 __all__ = ["EXPORTS", "LIB_PATH", "PaError", "Step", "load", "status_string", "alloc_workspace",
+           "copy_blocks",
            "decode", "decode_partitions", "decode_reduce", "partition_size",
            "reshape_and_cache", "workspace_size"]

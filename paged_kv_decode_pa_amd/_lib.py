@@ -18,7 +18,8 @@ STATUS = {0: "PA_OK", -1: "PA_EINVAL", -2: "PA_EUNSUPPORTED", -3: "PA_EWORKSPACE
 
 # every symbol include/pa.h declares
 EXPORTS = ("pa_status_string", "pa_reshape_and_cache", "pa_decode_partition_size",
-           "pa_decode_workspace_size", "pa_decode", "pa_decode_reduce", "pa_step",
+           "pa_decode_workspace_size", "pa_decode", "pa_decode_reduce", "pa_copy_blocks",
+           "pa_step",
            "pa_step_graph_create", "pa_step_graph_launch", "pa_step_graph_destroy")
 
 
@@ -71,6 +72,8 @@ def load() -> ctypes.CDLL:
                               i32, i32, i32, i32, i32, i32, f32, f32, i32, i32, i32, vp]
     lib.pa_decode_reduce.restype = i32
     lib.pa_decode_reduce.argtypes = [vp, vp, sz, vp, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.pa_copy_blocks.restype = i32
+    lib.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     sp = ctypes.POINTER(StepArgs)
     lib.pa_step.restype = i32
     lib.pa_step.argtypes = [sp, vp]

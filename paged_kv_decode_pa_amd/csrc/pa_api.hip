@@ -98,6 +98,22 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ELAUNCH;
 }
 
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int num_pairs,
+                   int num_blocks, int block_size, int num_kv_heads, int head_dim,
+                   pa_dtype dtype, void* stream) {
+  if (num_pairs < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PA_EINVAL;
+  if (!valid_dtype(dtype) || !supported_head_dim(head_dim) || !pow2_in(block_size, 1, 256))
+    return PA_EUNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_mapping) return PA_EINVAL;
+  const int64_t block16 = (int64_t)block_size * num_kv_heads * head_dim * elem_bytes(dtype) / 16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  pa::copy_blocks_kernel<<<dim3(num_pairs), dim3(256), 0, s>>>(
+      static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), block_mapping, num_blocks,
+      block16);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
 int pa_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                              int block_size, int max_context_len, int window, pa_dtype dtype) {
   (void)num_heads;

@@ -24,4 +24,22 @@ __global__ __launch_bounds__(256) void reshape_cache_kernel(
   }
 }
 
+// One workgroup per (src, dst) pair: 16-byte copies of a whole block of K
+// and of V.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(
+    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+    const int64_t* __restrict__ block_mapping, int64_t num_blocks, int64_t block16) {
+  const int64_t src = block_mapping[2 * (int64_t)blockIdx.x];
+  const int64_t dst = block_mapping[2 * (int64_t)blockIdx.x + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const uint4* ks = k_cache + src * block16;
+  const uint4* vs = v_cache + src * block16;
+  uint4* kd = k_cache + dst * block16;
+  uint4* vd = v_cache + dst * block16;
+  for (int64_t j = threadIdx.x; j < block16; j += blockDim.x) {
+    kd[j] = ks[j];
+    vd[j] = vs[j];
+  }
+}
+
 }  // namespace pa

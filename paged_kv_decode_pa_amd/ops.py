@@ -58,6 +58,20 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping) -> None:
         slot_mapping.data_ptr(), T, NB, bs, Hkv, D, _dt(key), _stream()))
 
 
+def copy_blocks(k_cache, v_cache, block_mapping) -> None:
+    """Copy whole blocks src -> dst in both caches, in place; block_mapping is
+    int64 [num_pairs, 2] of (src, dst) physical block ids."""
+    _dev(k_cache, v_cache, block_mapping)
+    if block_mapping.dtype != torch.int64 or block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be int64 [num_pairs, 2]")
+    if k_cache.dtype != v_cache.dtype or k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache must match")
+    NB, bs, Hkv, D = k_cache.shape
+    _lib.check("pa_copy_blocks", _lib.load().pa_copy_blocks(
+        k_cache.data_ptr(), v_cache.data_ptr(), block_mapping.data_ptr(),
+        block_mapping.shape[0], NB, bs, Hkv, D, _dt(k_cache), _stream()))
+
+
 def partition_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                    max_context_len, window=0, dtype=torch.bfloat16) -> int:
     """The library's choice of split-K partition size for a shape."""

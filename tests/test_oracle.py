@@ -414,3 +414,38 @@ def test_planted_mistakes_are_caught(name, monkeypatch):
         except AssertionError:
             failed += 1
     assert failed > 0, f"mutant {name!r} survived every pin"
+
+
+# --------------------------------------------------------------------------
+# copy_blocks (copy-on-write of shared blocks)
+# --------------------------------------------------------------------------
+def test_copy_blocks_slot_by_slot():
+    rng = np.random.default_rng(8)
+    NB, bs, Hkv, D = 9, 4, 2, 8
+    kc = encode(rng.standard_normal((NB, bs, Hkv, D)).astype(np.float32), "bf16")
+    vc = encode(rng.standard_normal((NB, bs, Hkv, D)).astype(np.float32), "bf16")
+    mapping = np.array([[0, 5], [3, 7], [12, 1], [2, -1]], dtype=np.int64)  # last two invalid
+    nk, nv = O.copy_blocks(kc, vc, mapping)
+    want_k, want_v = kc.copy(), vc.copy()
+    for src, dst in [(0, 5), (3, 7)]:
+        for t in range(bs):
+            for g in range(Hkv):
+                for d in range(D):
+                    want_k[dst, t, g, d] = kc[src, t, g, d]
+                    want_v[dst, t, g, d] = vc[src, t, g, d]
+    assert nk.tobytes() == want_k.tobytes() and nv.tobytes() == want_v.tobytes()
+
+
+def test_shared_prefix_blocks_decode_like_private_copies():
+    """Two sequences whose tables point at the same physical prefix blocks
+    attend exactly as if each owned a copy."""
+    c = make_case(B=2, Hq=4, Hkv=2, D=8, bs=4, dtype="f32", context_lens=[10, 13],
+                  seed=17, NB=12, order="identity")
+    # sequence 1 reuses sequence 0's first two blocks (positions 0..7)
+    shared = c.block_tables[0, :2].copy()
+    own = c.block_tables[1, :2].copy()
+    c.k_cache[own] = c.k_cache[shared]
+    c.v_cache[own] = c.v_cache[shared]
+    private = run(c)
+    c.block_tables[1, :2] = shared
+    assert np.array_equal(run(c), private)
