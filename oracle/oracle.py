@@ -1,4 +1,5 @@
-"""CPU oracle for single-query paged decode attention.
+"""CPU oracle for paged attention: one new query token per sequence (decode)
+or several (multi-query, causal among the new tokens).
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this module.  It shares no code
@@ -23,6 +24,11 @@ Definitions followed:
   * decode processes only the new token, so there is one query per sequence
     and its keys are positions [0, L) with L counting the new token (same
     README, "Key Concepts Explained: KV Cache");
+  * several new tokens per sequence (chunked prefill, speculative
+    verification: ovshake/nano-vllm README, "Features", "Advanced Scheduling"
+    and "Optimizations") are causal: each sees the keys up to its own
+    position (the self-attention chapter under that README's "Educational
+    Modes", on the triangular mask);
   * Gemma-2 logit soft-capping s -> c * tanh(s / c), applied after scaling,
     and a sliding window keeping the last W keys [max(0, L - W), L): the
     pages name Gemma 2 (flex-nano-vllm README, opening line) but print
@@ -116,10 +122,11 @@ def softmax_weighted_sum(s: np.ndarray, V: np.ndarray) -> np.ndarray:
     return (p @ V) / p.sum()
 
 
-def decode_sequence(q, k_cache, v_cache, block_tables, L, b, scale, softcap,
-                    window, dtype):
-    """float64 output [Hq, D] of sequence b."""
-    Hq, D = q.shape[1], q.shape[2]
+def attend(q_row, k_cache, v_cache, block_tables, b, L, scale, softcap, window,
+           dtype):
+    """float64 output [Hq, D] of one query token q_row [Hq, D] of sequence b
+    whose context is the sequence's positions [0, L) (window applied)."""
+    Hq, D = q_row.shape
     Hkv = k_cache.shape[2]
     G = Hq // Hkv
     out = np.zeros((Hq, D), dtype=np.float64)
@@ -128,13 +135,21 @@ def decode_sequence(q, k_cache, v_cache, block_tables, L, b, scale, softcap,
     start, end = attended_range(L, window)
     K = gather_sequence(k_cache, block_tables, b, start, end, dtype)
     V = gather_sequence(v_cache, block_tables, b, start, end, dtype)
-    qb = to_f64(q[b], dtype)
+    qb = to_f64(q_row, dtype)
     for h in range(Hq):
         g = kv_head_of(h, G)
         s = scale * (K[:, g, :] @ qb[h])
         s = cap(s, softcap)
         out[h] = softmax_weighted_sum(s, V[:, g, :])
     return out
+
+
+def decode_sequence(q, k_cache, v_cache, block_tables, L, b, scale, softcap,
+                    window, dtype):
+    """float64 output [Hq, D] of sequence b (its one query is the newest
+    token, so its context is all L positions)."""
+    return attend(q[b], k_cache, v_cache, block_tables, b, L, scale, softcap,
+                  window, dtype)
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale, softcap=0.0,
@@ -149,6 +164,49 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, softcap=0.0,
                                  int(context_lens[b]), b, scale, softcap,
                                  window, dtype)
     return out
+
+
+# --------------------------------------------------------------------------
+# multi-query attention (several new tokens per sequence)
+# --------------------------------------------------------------------------
+def query_positions(L: int, n: int) -> np.ndarray:
+    """Positions of a sequence's n new query tokens: the last n of its L
+    (context_lens counts every new token, as it counts the one new token of
+    a decode step)."""
+    return np.arange(L - n, L)
+
+
+def multi_query(q, query_start, k_cache, v_cache, block_tables, context_lens, scale,
+                softcap=0.0, window=0, dtype="f32"):
+    """float64 output [T, Hq, D] for T query tokens packed sequence by
+    sequence: rows query_start[b] .. query_start[b+1]-1 are sequence b's new
+    tokens in position order.  A token at position pos is causal: it sees
+    the keys at positions up to and including its own, i.e. it is the decode
+    query of a context of pos + 1 tokens (the window counts back from pos)."""
+    T, Hq, D = q.shape
+    if k_cache.shape[2] == 0 or Hq % k_cache.shape[2]:
+        raise ValueError("num query heads must be a multiple of num kv heads")
+    qs = np.asarray(query_start, dtype=np.int64)
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    for b in range(len(qs) - 1):
+        n = int(qs[b + 1] - qs[b])
+        L = int(context_lens[b])
+        if n > L:
+            raise ValueError("a sequence has more new tokens than context")
+        for i, pos in enumerate(query_positions(L, n)):
+            out[qs[b] + i] = attend(q[qs[b] + i], k_cache, v_cache, block_tables, b,
+                                    int(pos) + 1, scale, softcap, window, dtype)
+    return out
+
+
+def multi_query_case(case):
+    """Run the step a multi-query case describes: every new token's K/V row
+    lands first, then attention."""
+    kc, vc = case.k_cache, case.v_cache
+    if case.slot_mapping is not None:
+        kc, vc = reshape_and_cache(case.key, case.value, kc, vc, case.slot_mapping)
+    return multi_query(case.q, case.query_start, kc, vc, case.block_tables,
+                       case.context_lens, case.scale, case.softcap, case.window, case.dtype)
 
 
 def decode_case(case, seqs=None):

@@ -449,3 +449,160 @@ def test_shared_prefix_blocks_decode_like_private_copies():
     private = run(c)
     c.block_tables[1, :2] = shared
     assert np.array_equal(run(c), private)
+
+
+# --------------------------------------------------------------------------
+# multi-query attention (several new tokens per sequence, causal)
+# --------------------------------------------------------------------------
+from torch.nn.attention.bias import causal_lower_right  # noqa: E402
+
+from workloads import make_mq_case  # noqa: E402
+
+
+def widen_torch(bits, dtype):
+    """Stored values -> float64 tensor via torch's own dtype conversions."""
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(bits)).double()
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).double()
+
+
+def run_mq(c):
+    return O.multi_query(c.q, c.query_start, c.k_cache, c.v_cache, c.block_tables,
+                         c.context_lens, c.scale, c.softcap, c.window, c.dtype)
+
+
+def sdpa_rows(c, b, mask):
+    """Rows of sequence b by torch's scaled_dot_product_attention on the
+    gathered keys, KV heads widened with repeat_interleave."""
+    L = int(c.context_lens[b])
+    G = c.Hq // c.Hkv
+    K = widen_torch(gather_logical(c.k_cache, c.block_tables, c.context_lens)[b], c.dtype)
+    V = widen_torch(gather_logical(c.v_cache, c.block_tables, c.context_lens)[b], c.dtype)
+    q0, q1 = int(c.query_start[b]), int(c.query_start[b + 1])
+    qb = widen_torch(c.q[q0:q1], c.dtype)                       # [n, Hq, D]
+    K = K.repeat_interleave(G, dim=1).transpose(0, 1).contiguous()  # [Hq, L, D]
+    V = V.repeat_interleave(G, dim=1).transpose(0, 1).contiguous()
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qb.transpose(0, 1).contiguous(), K, V, attn_mask=mask(q1 - q0, L), scale=c.scale)
+    return o.transpose(0, 1).numpy()
+
+
+def mq_small(dtype="f32", **kw):
+    base = dict(Hq=4, Hkv=2, D=8, bs=4, dtype=dtype, context_lens=[7, 13, 27, 5],
+                query_lens=[3, 13, 6, 1], seed=23)
+    base.update(kw)
+    return make_mq_case(**base)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_mq_matches_sdpa_lower_right_causal(dtype):
+    """New tokens are the last n positions: torch's bottom-right causal mask."""
+    c = mq_small(dtype, scale=0.6)
+    got = run_mq(c)
+    for b in range(c.B):
+        want = sdpa_rows(c, b, lambda n, L: causal_lower_right(n, L)._materialize())
+        q0, q1 = c.query_start[b], c.query_start[b + 1]
+        np.testing.assert_allclose(got[q0:q1], want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("W", [1, 4, 9])
+def test_mq_window_matches_banded_sdpa(W):
+    c = mq_small("bf16", window=W, scale=0.6)
+    got = run_mq(c)
+
+    def band(n, L):
+        rows = torch.arange(L - n, L)[:, None]
+        cols = torch.arange(L)[None, :]
+        return (cols <= rows) & (cols > rows - W)
+
+    for b in range(c.B):
+        q0, q1 = c.query_start[b], c.query_start[b + 1]
+        np.testing.assert_allclose(got[q0:q1], sdpa_rows(c, b, band), rtol=0, atol=1e-12)
+
+
+def brute_mq(c):
+    """Token-by-token walk with math.exp / math.tanh; every new token
+    attends to the positions up to its own (window counted back from it)."""
+    G = c.Hq // c.Hkv
+    widened = [g for g in range(c.Hkv) for _ in range(G)]
+    out = np.zeros((c.T, c.Hq, c.D))
+    for b in range(c.B):
+        L = int(c.context_lens[b])
+        q0, q1 = int(c.query_start[b]), int(c.query_start[b + 1])
+        for r in range(q0, q1):
+            pos = L - (q1 - q0) + (r - q0)
+            first = 0 if c.window <= 0 else max(0, pos + 1 - c.window)
+            for h in range(c.Hq):
+                g = widened[h]
+                qv = [py_value(c.q[r, h, d], c.dtype) for d in range(c.D)]
+                scores, rows = [], []
+                for t in range(first, pos + 1):
+                    phys = int(c.block_tables[b][t // c.bs])
+                    slot = t - (t // c.bs) * c.bs
+                    k = [py_value(c.k_cache[phys, slot, g, d], c.dtype) for d in range(c.D)]
+                    v = [py_value(c.v_cache[phys, slot, g, d], c.dtype) for d in range(c.D)]
+                    s = c.scale * sum(a * x for a, x in zip(qv, k))
+                    if c.softcap > 0:
+                        s = c.softcap * math.tanh(s / c.softcap)
+                    scores.append(s)
+                    rows.append(v)
+                top = max(scores)
+                w = [math.exp(s - top) for s in scores]
+                tot = sum(w)
+                for d in range(c.D):
+                    out[r, h, d] = sum(wi * row[d] for wi, row in zip(w, rows)) / tot
+    return out
+
+
+@pytest.mark.parametrize("softcap,window", [(2.0, 0), (1.5, 6)])
+def test_mq_brute_force_softcap_gqa(softcap, window):
+    c = mq_small("bf16", Hq=8, Hkv=2, softcap=softcap, window=window, scale=0.9,
+                 context_lens=[9, 14, 4], query_lens=[4, 14, 0])
+    np.testing.assert_allclose(run_mq(c), brute_mq(c), rtol=0, atol=1e-12)
+
+
+def test_mq_one_new_token_is_decode():
+    c = mq_small("f16", query_lens=[1, 1, 1, 1], softcap=5.0, window=8)
+    dec = O.decode(c.q, c.k_cache, c.v_cache, c.block_tables, c.context_lens, c.scale,
+                   c.softcap, c.window, c.dtype)
+    assert np.array_equal(run_mq(c), dec)
+
+
+def test_mq_no_new_tokens():
+    c = mq_small("f32", query_lens=[0, 0, 0, 0])
+    assert run_mq(c).shape == (0, 4, 8)
+
+
+def test_mq_last_row_sees_the_whole_context():
+    """The newest token of a sequence attends to all of it, whatever the
+    number of new tokens before it."""
+    c = mq_small("bf16", query_lens=[7, 13, 1, 5], context_lens=[7, 13, 27, 5])
+    got = run_mq(c)
+    for b in range(c.B):
+        last = int(c.query_start[b + 1]) - 1
+        q1 = c.q[last][None]
+        want = O.attend(q1[0], c.k_cache, c.v_cache, c.block_tables, b,
+                        int(c.context_lens[b]), c.scale, 0.0, 0, c.dtype)
+        assert np.array_equal(got[last], want)
+
+
+MQ_MUTANTS = {
+    "causal from the top": ("query_positions", lambda L, n: np.arange(0, n)),
+    "causal off by one": ("query_positions", lambda L, n: np.arange(L - n - 1, L - 1)),
+    "newest token first": ("query_positions", lambda L, n: np.arange(L - n, L)[::-1]),
+}
+
+
+@pytest.mark.parametrize("name", list(MQ_MUTANTS))
+def test_mq_planted_mistakes_are_caught(name, monkeypatch):
+    attr, fn = MQ_MUTANTS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failed = 0
+    for pin in (lambda: test_mq_matches_sdpa_lower_right_causal("f32"),
+                lambda: test_mq_window_matches_banded_sdpa(4)):
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            failed += 1
+    assert failed > 0, f"mutant {name!r} survived every pin"

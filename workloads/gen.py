@@ -322,3 +322,184 @@ def workload(n: int, poison: bool = True, partition_size: Optional[int] = None) 
         raise ValueError(n)
     c.name = WORKLOADS[n]
     return c
+
+
+# --------------------------------------------------------------------------
+# multi-query cases: several new tokens per sequence
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class MQCase:
+    name: str
+    dtype: str
+    q: np.ndarray              # [T, Hq, D] storage, tokens packed sequence by sequence
+    query_start: np.ndarray    # [B+1] int32: sequence b owns rows query_start[b] .. [b+1]-1
+    k_cache: np.ndarray        # [NB, bs, Hkv, D] storage (state before the new rows land)
+    v_cache: np.ndarray
+    block_tables: np.ndarray   # [B, max_blocks] int32
+    context_lens: np.ndarray   # [B] int32, counts every new token
+    scale: float
+    softcap: float
+    window: int
+    partition_size: Optional[int]
+    key: Optional[np.ndarray] = None           # [T, Hkv, D] new rows of the new tokens
+    value: Optional[np.ndarray] = None
+    slot_mapping: Optional[np.ndarray] = None  # [T] int64
+
+    @property
+    def B(self):
+        return self.context_lens.shape[0]
+
+    @property
+    def T(self):
+        return self.q.shape[0]
+
+    @property
+    def Hq(self):
+        return self.q.shape[1]
+
+    @property
+    def D(self):
+        return self.q.shape[2]
+
+    @property
+    def NB(self):
+        return self.k_cache.shape[0]
+
+    @property
+    def bs(self):
+        return self.k_cache.shape[1]
+
+    @property
+    def Hkv(self):
+        return self.k_cache.shape[2]
+
+    @property
+    def query_lens(self):
+        return np.diff(self.query_start.astype(np.int64))
+
+    @property
+    def max_context_len(self):
+        return int(self.context_lens.max()) if self.B else 0
+
+    @property
+    def max_query_len(self):
+        return int(self.query_lens.max()) if self.B else 0
+
+    def algorithmic_bytes(self) -> dict:
+        """K/V rows of the union of the keys a sequence's new tokens attend
+        to (read once), q read + out write, table entries, lengths and
+        offsets; plus the new rows written by reshape_and_cache."""
+        eb = ELEM_BYTES[self.dtype]
+        L = self.context_lens.astype(np.int64)
+        n = self.query_lens
+        first = L - n  # position of the first new token
+        lo = np.maximum(0, first + 1 - self.window) if self.window > 0 else np.zeros_like(L)
+        keys = np.where(n > 0, L - lo, 0)
+        pages = np.where(n > 0, (L - 1) // self.bs - lo // self.bs + 1, 0)
+        kv = int(keys.sum()) * self.Hkv * self.D * eb * 2
+        qo = 2 * self.T * self.Hq * self.D * eb
+        meta = int(pages.sum()) * 4 + 4 * self.B + 4 * (self.B + 1)
+        rc = 0
+        if self.slot_mapping is not None:
+            rc = 2 * 2 * self.T * self.Hkv * self.D * eb + 8 * self.T
+        return {"kv": kv, "q_out": qo, "meta": meta, "attn": kv + qo + meta,
+                "reshape": rc, "total": kv + qo + meta + rc}
+
+    def flops(self) -> int:
+        """4 * D flops (q.k and p.v) per (query head, attended key) pair."""
+        L = self.context_lens.astype(np.int64)
+        tot = 0
+        for b in range(self.B):
+            n = int(self.query_lens[b])
+            pos = np.arange(L[b] - n, L[b])
+            keys = pos + 1 if self.window <= 0 else np.minimum(pos + 1, self.window)
+            tot += int(keys.sum())
+        return 4 * self.D * self.Hq * tot
+
+
+def make_mq_case(*, Hq: int, Hkv: int, D: int, bs: int, dtype: str,
+                 context_lens: Sequence[int], query_lens: Sequence[int],
+                 NB: Optional[int] = None, scale: Optional[float] = None,
+                 softcap: float = 0.0, window: int = 0,
+                 partition_size: Optional[int] = 0, seed: int = 0,
+                 new_rows: bool = False, poison: bool = True,
+                 order: str = "shuffled", name: str = "custom-mq") -> MQCase:
+    """A multi-query case: sequence b holds context_lens[b] tokens, of which
+    the last query_lens[b] are new (their queries are q's rows, in position
+    order).  The cache comes from ``make_case`` with the same seed; q and the
+    new rows are drawn from streams 5 and 6 of SeedSequence(seed).spawn(7)."""
+    L = np.asarray(context_lens, dtype=np.int32)
+    n = np.asarray(query_lens, dtype=np.int32)
+    assert L.shape == n.shape and (n <= L).all() and (n >= 0).all()
+    B = L.shape[0]
+    base = make_case(B=B, Hq=Hq, Hkv=Hkv, D=D, bs=bs, dtype=dtype, context_lens=L, NB=NB,
+                     scale=scale, softcap=softcap, window=window,
+                     partition_size=partition_size, seed=seed, poison=poison, order=order)
+    ss = np.random.SeedSequence(seed).spawn(7)
+    r_q, r_new = np.random.default_rng(ss[5]), np.random.default_rng(ss[6])
+    qs = np.zeros(B + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(n)
+    T = int(qs[-1])
+    q = encode(r_q.standard_normal((T, Hq, D), dtype=np.float32), dtype)
+    kc, vc = base.k_cache, base.v_cache
+    key = value = slots = None
+    if new_rows:
+        key = encode(r_new.standard_normal((T, Hkv, D), dtype=np.float32), dtype)
+        value = encode(r_new.standard_normal((T, Hkv, D), dtype=np.float32), dtype)
+        slots = np.empty(T, dtype=np.int64)
+        for b in range(B):
+            for i in range(int(n[b])):
+                pos = int(L[b]) - int(n[b]) + i
+                blk, off = int(base.block_tables[b, pos // bs]), pos % bs
+                slots[qs[b] + i] = blk * bs + off
+                kc[blk, off] = poison_fill((Hkv, D), dtype)
+                vc[blk, off] = poison_fill((Hkv, D), dtype)
+    return MQCase(name=name, dtype=dtype, q=q, query_start=qs, k_cache=kc, v_cache=vc,
+                  block_tables=base.block_tables, context_lens=L, scale=base.scale,
+                  softcap=base.softcap, window=base.window, partition_size=partition_size,
+                  key=key, value=value, slot_mapping=slots)
+
+
+MQ_WORKLOADS = {
+    "spec5": "gemma2-2b-spec-verify5-bf16-b512",
+    "chunk512": "gemma2-2b-chunked-prefill512-bf16",
+    "prefill": "llama-gqa8-prefill-f16",
+}
+
+
+def mq_workload(name: str, poison: bool = True,
+                partition_size: Optional[int] = None) -> MQCase:
+    """Named multi-query workloads at full size.
+
+    spec5    the Gemma-2 serving batch of workload 4 (512 sequences, lengths
+             17..1024) verifying 5 speculative tokens each (the pages'
+             speculative-decoding example uses 5);
+    chunk512 one 512-token chunk of a 4096-token Gemma-2 prompt (the pages'
+             default chunked-prefill budget is 512 tokens) batched with 63
+             decoding sequences of workload 2's lengths;
+    prefill  4 prompts of 2048 tokens each, prefilled whole (f16, 32/4
+             heads, head_dim 64, block 32), every K/V row landing in the
+             cache first."""
+    if name == "spec5":
+        L = workload_lengths(4)
+        n = np.full(L.shape, 5, dtype=np.int32)
+        L = np.maximum(L, 5)
+        c = make_mq_case(Hq=8, Hkv=4, D=256, bs=16, dtype="bf16", context_lens=L,
+                         query_lens=n, NB=40000, scale=1 / 16, softcap=50.0, seed=1101,
+                         poison=poison, new_rows=True, partition_size=partition_size)
+    elif name == "chunk512":
+        Ld = workload_lengths(2)[:63]
+        L = np.concatenate([[4096], Ld]).astype(np.int32)
+        n = np.concatenate([[512], np.ones(63, dtype=np.int32)]).astype(np.int32)
+        c = make_mq_case(Hq=8, Hkv=4, D=256, bs=16, dtype="bf16", context_lens=L,
+                         query_lens=n, NB=8192, scale=1 / 16, softcap=50.0, seed=1102,
+                         poison=poison, new_rows=True, partition_size=partition_size)
+    elif name == "prefill":
+        L = np.full(4, 2048, dtype=np.int32)
+        c = make_mq_case(Hq=32, Hkv=4, D=64, bs=32, dtype="f16", context_lens=L,
+                         query_lens=L, scale=1 / 8, seed=1103, poison=poison,
+                         new_rows=True, partition_size=partition_size)
+    else:
+        raise ValueError(name)
+    c.name = MQ_WORKLOADS[name]
+    return c
