@@ -162,6 +162,48 @@ int pa_decode_reduce(void* out, const void* workspace, size_t workspace_bytes,
                      void* stream);
 
 /*
+ * Multi-query attention: a sequence brings n_b >= 0 new tokens at once, the
+ * last n_b of its context_lens[b] positions (a prompt chunk under chunked
+ * prefill, or the draft tokens a speculative-decoding step verifies:
+ * ovshake/nano-vllm README, "Features", "Advanced Scheduling" and
+ * "Optimizations").  Attention is causal (the self-attention chapter under
+ * that README's "Educational Modes"): the new token at position
+ * pos = L_b - n_b + i attends to the keys at [max(0, pos+1-window), pos]
+ * (window 0: [0, pos]) with the decode rule above, so n_b = 1 is decode and
+ * n_b = L_b is the prefill of a whole prompt.  Every new token's K/V row must
+ * already be in the cache (pa_reshape_and_cache first).  One call enqueues
+ * the plan, the attention pass and, when keys are split, the reduce.
+ *   q, out        [num_tokens, num_heads, head_dim], tokens packed sequence
+ *                 by sequence in position order
+ *   query_start   [num_seqs + 1] int32: sequence b owns rows
+ *                 query_start[b] .. query_start[b+1]-1; query_start[0] = 0,
+ *                 non-decreasing, query_start[num_seqs] = num_tokens
+ *   context_lens  [num_seqs] int32, counting all new tokens (n_b <= L_b)
+ *   max_query_len host-side hint >= 1 (the largest n_b); it picks the tile
+ *                 shape only, results do not depend on it
+ *   partition_size  0, or a positive multiple of block_size
+ * The query_start contract and n_b <= L_b <= max_context_len are device-side
+ * contracts (not checked).  Supported: as pa_decode, and any group size
+ * for f16/bf16 with block_size >= 16 (matrix-core path; other shapes run
+ * each token through the decode kernels).
+ */
+int pa_mq_partition_size(int num_seqs, int num_tokens, int max_query_len, int num_heads,
+                         int num_kv_heads, int head_dim, int block_size, int max_context_len,
+                         int window, pa_dtype dtype);
+
+/* Bytes of workspace pa_mq_attention needs (0 when num_tokens <= 0). */
+size_t pa_mq_workspace_size(int num_seqs, int num_tokens, int num_heads, int num_kv_heads,
+                            int head_dim, int max_context_len, int partition_size);
+
+int pa_mq_attention(void* out, void* workspace, size_t workspace_bytes, const void* q,
+                    const int32_t* query_start, int num_tokens, int max_query_len,
+                    const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                    int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+                    int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                    int num_blocks, float scale, float softcap, int window, int partition_size,
+                    pa_dtype dtype, void* stream);
+
+/*
  * One layer-step: pa_reshape_and_cache (when num_tokens > 0), pa_decode and
  * pa_decode_reduce with the arguments below, on one stream.  The step can
  * also be captured once into a HIP graph and replayed: static graph execution

@@ -6,9 +6,10 @@ torch's current stream into those calls.
 """
 from ._lib import EXPORTS, LIB_PATH, PaError, load, status_string
 from .ops import (Step, alloc_workspace, copy_blocks, decode, decode_partitions, decode_reduce,
-                  partition_size, reshape_and_cache, workspace_size)
+                  mq_attention, mq_partition_size, mq_workspace_size, partition_size,
+                  reshape_and_cache, workspace_size)
 
 __all__ = ["EXPORTS", "LIB_PATH", "PaError", "Step", "load", "status_string", "alloc_workspace",
-           "copy_blocks",
+           "copy_blocks", "mq_attention", "mq_partition_size", "mq_workspace_size",
            "decode", "decode_partitions", "decode_reduce", "partition_size",
            "reshape_and_cache", "workspace_size"]

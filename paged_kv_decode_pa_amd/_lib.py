@@ -19,7 +19,7 @@ STATUS = {0: "PA_OK", -1: "PA_EINVAL", -2: "PA_EUNSUPPORTED", -3: "PA_EWORKSPACE
 # every symbol include/pa.h declares
 EXPORTS = ("pa_status_string", "pa_reshape_and_cache", "pa_decode_partition_size",
            "pa_decode_workspace_size", "pa_decode", "pa_decode_reduce", "pa_copy_blocks",
-           "pa_step",
+           "pa_mq_partition_size", "pa_mq_workspace_size", "pa_mq_attention", "pa_step",
            "pa_step_graph_create", "pa_step_graph_launch", "pa_step_graph_destroy")
 
 
@@ -74,6 +74,13 @@ def load() -> ctypes.CDLL:
     lib.pa_decode_reduce.argtypes = [vp, vp, sz, vp, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.pa_copy_blocks.restype = i32
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.pa_mq_partition_size.restype = i32
+    lib.pa_mq_partition_size.argtypes = [i32] * 10
+    lib.pa_mq_workspace_size.restype = sz
+    lib.pa_mq_workspace_size.argtypes = [i32] * 7
+    lib.pa_mq_attention.restype = i32
+    lib.pa_mq_attention.argtypes = [vp, vp, sz, vp, vp, i32, i32, vp, vp, vp, i32, vp, i32,
+                                    i32, i32, i32, i32, i32, i32, f32, f32, i32, i32, i32, vp]
     sp = ctypes.POINTER(StepArgs)
     lib.pa_step.restype = i32
     lib.pa_step.argtypes = [sp, vp]

@@ -159,12 +159,14 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim, int m
          partials_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size);
 }
 
-int pa_decode(void* out, void* workspace, size_t workspace_bytes, const void* q,
-              const void* k_cache, const void* v_cache, const int32_t* block_tables,
-              int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
-              int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
-              int num_blocks, float scale, float softcap, int window, int partition_size,
-              pa_dtype dtype, void* stream) {
+// pa_decode with an optional table-row map (multi-query launches run each
+// query token as a sequence of its own; see pa_mq_attention).
+static int decode_impl(void* out, void* workspace, size_t workspace_bytes, const void* q,
+                       const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                       int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+                       int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                       int num_blocks, float scale, float softcap, int window, int partition_size,
+                       pa_dtype dtype, void* stream, const int32_t* seq_row) {
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
       max_blocks_per_seq <= 0 || max_context_len < 0 || window < 0 || partition_size < 0)
     return PA_EINVAL;
@@ -211,6 +213,7 @@ int pa_decode(void* out, void* workspace, size_t workspace_bytes, const void* q,
   p.v_cache = v_cache;
   p.block_tables = block_tables;
   p.context_lens = context_lens;
+  p.seq_row = seq_row;
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.max_context_len = max_context_len;
   p.num_seqs = num_seqs;
@@ -271,6 +274,18 @@ int pa_decode(void* out, void* workspace, size_t workspace_bytes, const void* q,
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ELAUNCH;
 }
 
+int pa_decode(void* out, void* workspace, size_t workspace_bytes, const void* q,
+              const void* k_cache, const void* v_cache, const int32_t* block_tables,
+              int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+              int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+              int num_blocks, float scale, float softcap, int window, int partition_size,
+              pa_dtype dtype, void* stream) {
+  return decode_impl(out, workspace, workspace_bytes, q, k_cache, v_cache, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, scale, softcap, window,
+                     partition_size, dtype, stream, nullptr);
+}
+
 int pa_decode_reduce(void* out, const void* workspace, size_t workspace_bytes,
                      const int32_t* context_lens, int max_context_len, int num_seqs,
                      int num_heads, int head_dim, int partition_size, int window,
@@ -318,6 +333,196 @@ int pa_decode_reduce(void* out, const void* workspace, size_t workspace_bytes,
   }
 #undef PA_REDUCE_CASE
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
+// ---------------------------------------------------------------------------
+// multi-query attention
+// ---------------------------------------------------------------------------
+// The tiled path takes 16-bit KV in pages of 16+ tokens; PA_MQ_TILED=0 forces
+// the per-token path.
+static bool mq_tiled(int dtype, int block_size, int max_query_len) {
+  return (dtype == PA_F16 || dtype == PA_BF16) && block_size >= 16 && max_query_len > 1 &&
+         env_int("PA_MQ_TILED", 1) != 0;
+}
+
+// 16-row blocks per wavefront: enough for a sequence's max_query_len * G
+// rows, up to what the registers hold for the head size.
+static int mq_row_blocks(int head_dim, int G, int max_query_len) {
+  const int cap = head_dim == 64 ? 4 : head_dim == 128 ? 2 : 1;
+  const long rows = (long)max_query_len * G;
+  int nr = 1;
+  while (nr < cap && 16L * nr < rows) nr *= 2;
+  return nr;
+}
+
+// Tiles of R rows over every sequence's n * G rows: at most one partial tile
+// per sequence, and never more tiles than rows.
+static long mq_max_tiles(int num_seqs, int num_tokens, int G, int R) {
+  const long rows = (long)num_tokens * G;
+  const long t = rows / R + num_seqs;
+  return t < rows ? t : rows;
+}
+
+// Workspace: vctx [T], vrow [T], tiles [max tiles at R = 16] int32 pairs,
+// the tile count, then a decode workspace for T sequences.
+static size_t mq_head_bytes(int num_seqs, int num_tokens, int G) {
+  return 2 * pad256((size_t)num_tokens * 4) +
+         pad256((size_t)mq_max_tiles(num_seqs, num_tokens, G, 16) * 8) + 256;
+}
+
+int pa_mq_partition_size(int num_seqs, int num_tokens, int max_query_len, int num_heads,
+                         int num_kv_heads, int head_dim, int block_size, int max_context_len,
+                         int window, pa_dtype dtype) {
+  if (num_seqs <= 0 || num_tokens <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads ||
+      block_size <= 0 || max_context_len <= 0 || max_query_len <= 0)
+    return 0;
+  int forced = env_int("PA_DECODE_PARTITION", -1);
+  if (forced >= 0) return forced;
+  const int G = num_heads / num_kv_heads;
+  long units;
+  if (mq_tiled(dtype, block_size, max_query_len)) {
+    const int R = 16 * mq_row_blocks(head_dim, G, max_query_len);
+    units = mq_max_tiles(num_seqs, num_tokens, G, R) * num_kv_heads;
+  } else {
+    units = (long)num_tokens * num_kv_heads;
+  }
+  const int span = window > 0 ? (window < max_context_len ? window : max_context_len)
+                              : max_context_len;
+  if (units >= 4L * kNumCUs && span <= 2048) return 0;
+  int part = 512;
+  if (part % block_size) part = block_size;
+  return part;
+}
+
+size_t pa_mq_workspace_size(int num_seqs, int num_tokens, int num_heads, int num_kv_heads,
+                            int head_dim, int max_context_len, int partition_size) {
+  if (num_seqs <= 0 || num_tokens <= 0 || num_heads <= 0 || num_kv_heads <= 0 ||
+      num_heads % num_kv_heads || head_dim <= 0 || partition_size < 0)
+    return 0;
+  return mq_head_bytes(num_seqs, num_tokens, num_heads / num_kv_heads) +
+         pa_decode_workspace_size(num_tokens, num_heads, head_dim, max_context_len,
+                                  partition_size);
+}
+
+int pa_mq_attention(void* out, void* workspace, size_t workspace_bytes, const void* q,
+                    const int32_t* query_start, int num_tokens, int max_query_len,
+                    const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                    int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+                    int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                    int num_blocks, float scale, float softcap, int window, int partition_size,
+                    pa_dtype dtype, void* stream) {
+  if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
+      num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || window < 0 ||
+      partition_size < 0)
+    return PA_EINVAL;
+  if (num_heads % num_kv_heads) return PA_EINVAL;
+  if (num_tokens > 0 && (num_seqs == 0 || max_query_len < 1 || max_query_len > num_tokens))
+    return PA_EINVAL;
+  if (!isfinite(scale) || !(softcap >= 0.0f) || !isfinite(softcap)) return PA_EINVAL;
+  if (!valid_dtype(dtype) || !supported_head_dim(head_dim) || !pow2_in(block_size, 1, 256))
+    return PA_EUNSUPPORTED;
+  if (partition_size > 0 && partition_size % block_size) return PA_EINVAL;
+  if ((long)max_context_len > (long)max_blocks_per_seq * block_size) return PA_EINVAL;
+  if (num_tokens == 0) return PA_OK;
+  if (!out || !q || !query_start || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PA_EINVAL;
+  const int G = num_heads / num_kv_heads;
+  const bool tiled = mq_tiled(dtype, block_size, max_query_len);
+  if (!tiled) {
+    // the per-token path takes what the decode kernels take
+    const bool mfma = (dtype == PA_F16 || dtype == PA_BF16) && (G == 8 || G == 16) &&
+                      block_size >= 16 && env_int("PA_DECODE_MFMA", 1) != 0;
+    if (!(G == 1 || G == 2 || G == 4 || G == 8 || (G == 16 && mfma))) return PA_EUNSUPPORTED;
+  }
+  const size_t need = pa_mq_workspace_size(num_seqs, num_tokens, num_heads, num_kv_heads,
+                                           head_dim, max_context_len, partition_size);
+  if (!workspace || workspace_bytes < need) return PA_EWORKSPACE;
+
+  char* wsb = static_cast<char*>(workspace);
+  int32_t* vctx = reinterpret_cast<int32_t*>(wsb);
+  int32_t* vrow = reinterpret_cast<int32_t*>(wsb + pad256((size_t)num_tokens * 4));
+  int2* tiles = reinterpret_cast<int2*>(wsb + 2 * pad256((size_t)num_tokens * 4));
+  int32_t* num_tiles = reinterpret_cast<int32_t*>(
+      wsb + 2 * pad256((size_t)num_tokens * 4) +
+      pad256((size_t)mq_max_tiles(num_seqs, num_tokens, G, 16) * 8));
+  char* dws = wsb + mq_head_bytes(num_seqs, num_tokens, G);
+  const size_t dws_bytes = workspace_bytes - mq_head_bytes(num_seqs, num_tokens, G);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  const int nr = tiled ? mq_row_blocks(head_dim, G, max_query_len) : 1;
+  const int R = 16 * nr;
+  pa::mq_plan_kernel<<<dim3(1), dim3(1024), 0, s>>>(
+      query_start, context_lens, num_seqs, num_tokens, max_context_len, G, R,
+      tiled ? tiles : nullptr, (int)mq_max_tiles(num_seqs, num_tokens, G, R), num_tiles, vctx,
+      tiled ? nullptr : vrow);
+  if (hipGetLastError() != hipSuccess) return PA_ELAUNCH;
+
+  int rc;
+  if (!tiled) {
+    // every query token is a decode sequence of context pos + 1
+    rc = decode_impl(out, dws, dws_bytes, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                     vctx, max_context_len, num_tokens, num_heads, num_kv_heads, head_dim,
+                     block_size, num_blocks, scale, softcap, window, partition_size, dtype,
+                     stream, vrow);
+  } else {
+    const int np = num_parts(max_context_len, partition_size);
+    pa::MQParams p{};
+    p.out = out;
+    if (partials_bytes(num_tokens, num_heads, head_dim, max_context_len, partition_size)) {
+      const size_t rows = (size_t)num_tokens * num_heads * np;
+      float* ws = reinterpret_cast<float*>(dws + plan_bytes(num_tokens, max_context_len,
+                                                            partition_size));
+      p.tmp_out = ws;
+      p.max_logits = ws + rows * head_dim;
+      p.exp_sums = p.max_logits + rows;
+    }
+    p.tiles = tiles;
+    p.num_tiles = num_tiles;
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_tables = block_tables;
+    p.context_lens = context_lens;
+    p.query_start = query_start;
+    p.max_blocks_per_seq = max_blocks_per_seq;
+    p.max_context_len = max_context_len;
+    p.num_heads = num_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = G;
+    p.num_blocks = num_blocks;
+    p.log2_bs = ilog2(block_size);
+    p.window = window;
+    p.part = partition_size > 0 ? partition_size : (max_context_len > 0 ? max_context_len : 1);
+    p.num_parts = np;
+    if (softcap > 0.0f) {
+      p.qk_mul = scale / softcap;
+      p.cap_mul = softcap * pa::kLog2e;
+    } else {
+      p.qk_mul = scale * pa::kLog2e;
+      p.cap_mul = 0.0f;
+    }
+    const long max_tiles = mq_max_tiles(num_seqs, num_tokens, G, R);
+    p.max_tiles = (int)max_tiles;
+    p.num_tokens = num_tokens;
+    const long blocks = max_tiles * num_kv_heads * np;
+    if (blocks > 0x7fffffffL) return PA_EUNSUPPORTED;
+    const int tiles_per_chunk = block_size >= 32 && nr * head_dim <= 128 ? 2 : 1;
+    const size_t lds_wave = pa::mq_mfma_lds_bytes(head_dim, nr, tiles_per_chunk);
+    const int span = window > 0 && window < p.part ? window : p.part;
+    int nw = waves_for(span, 16 * tiles_per_chunk, (int)(blocks < (1L << 30) ? blocks : (1L << 30)));
+    while (nw > 1 && nw * lds_wave > 65536) nw /= 2;
+    const dim3 grid((unsigned)blocks);
+    const bool ok =
+        dtype == PA_F16
+            ? pa::launch_mq_mfma_f16(head_dim, nr, tiles_per_chunk, nw, grid, s, p)
+            : pa::launch_mq_mfma_bf16(head_dim, nr, tiles_per_chunk, nw, grid, s, p);
+    if (!ok) return PA_EUNSUPPORTED;
+    rc = hipGetLastError() == hipSuccess ? PA_OK : PA_ELAUNCH;
+  }
+  if (rc != PA_OK) return rc;
+  // split-K partials of tokens whose keys span several partitions
+  return pa_decode_reduce(out, dws, dws_bytes, vctx, max_context_len, num_tokens, num_heads,
+                          head_dim, partition_size, window, dtype, stream);
 }
 
 }  // extern "C"

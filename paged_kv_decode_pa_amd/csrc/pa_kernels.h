@@ -42,6 +42,7 @@ struct DecodeParams {
   const void* v_cache;
   const int32_t* block_tables;  // [B, max_blocks_per_seq]
   const int32_t* context_lens;  // [B]
+  const int32_t* seq_row;  // null, or [B] block-table row of each unit sequence
   int max_blocks_per_seq;
   int max_context_len;
   int num_seqs;
@@ -87,6 +88,15 @@ struct DecodeShape {
   static_assert(LPR >= 2 && LPR <= 64, "row must span 2..64 lanes");
   static_assert((G & (G - 1)) == 0 && G <= 64, "group size must be a power of two");
 };
+
+// Block-table row of sequence b.  Multi-query launches run every query token
+// as its own sequence (context = the keys up to the token's position), all
+// of one sequence's tokens sharing its table row through seq_row.
+__device__ __forceinline__ const int32_t* table_row(const DecodeParams& p, int b) {
+  typedef const __attribute__((address_space(4))) int32_t cint32;
+  const int row = p.seq_row ? ((cint32*)p.seq_row)[b] : b;
+  return p.block_tables + (size_t)row * p.max_blocks_per_seq;
+}
 
 // The (sequence, KV head, partition) unit of a decode workgroup.
 struct Unit {
@@ -238,7 +248,7 @@ __global__ __launch_bounds__(64 * kMaxWaves, PA_DECODE_MIN_WAVES) void decode_ke
   // A window of 64 consecutive block-table entries per wavefront, in LDS.
   // Refilled (rarely: every 64 pages) inside a uniform branch, so the wait
   // for the refill never holds back the K/V loads already in flight.
-  const int32_t* bt = p.block_tables + (size_t)b * p.max_blocks_per_seq;
+  const int32_t* bt = table_row(p, b);
   const int log2_bs = p.log2_bs;
   const int last_pg = (hi - 1) >> log2_bs;
   int pg0 = -(1 << 30);

@@ -5,6 +5,7 @@
 
 #include "pa_kernels.h"
 #include "pa_mfma.h"
+#include "pa_mq.h"
 
 namespace pa {
 
@@ -20,6 +21,14 @@ bool launch_decode_mfma_f16(int D, int G, int tiles, bool loop, int nw, dim3 gri
 bool launch_decode_mfma_bf16(int D, int G, int tiles, bool loop, int nw, dim3 grid, hipStream_t s,
                              const DecodeParams& p);
 size_t decode_mfma_lds_bytes(int D, int G, int tiles);
+
+// Tiled multi-query path (f16/bf16, block_size >= 16 * tiles); nr 16-row
+// blocks per wavefront.  Returns false when not built for the shape.
+bool launch_mq_mfma_f16(int D, int nr, int tiles, int nw, dim3 grid, hipStream_t s,
+                        const MQParams& p);
+bool launch_mq_mfma_bf16(int D, int nr, int tiles, int nw, dim3 grid, hipStream_t s,
+                         const MQParams& p);
+size_t mq_mfma_lds_bytes(int D, int nr, int tiles);
 
 }  // namespace pa
 
@@ -69,6 +78,29 @@ size_t decode_mfma_lds_bytes(int D, int G, int tiles);
       PA_MFMA_CASE(DT, 64, 16, 1) PA_MFMA_CASE(DT, 64, 16, 2)                       \
       PA_MFMA_CASE(DT, 128, 16, 1) PA_MFMA_CASE(DT, 128, 16, 2)                     \
       PA_MFMA_CASE(DT, 256, 16, 1) PA_MFMA_CASE(DT, 256, 16, 2)                     \
+      default: return false;                                                        \
+    }                                                                               \
+  }
+
+#define PA_MQ_CASE(DT, DV, NRV, TV)                                                 \
+  case (DV * 8 + NRV) * 4 + TV: {                                                   \
+    const size_t lds = (size_t)nw * sizeof(float) * MQShape<DT, DV, NRV, TV>::LDS_FLOATS; \
+    mq_mfma_kernel<DT, DV, NRV, TV><<<grid, dim3(64 * nw), lds, s>>>(p);             \
+    return true;                                                                    \
+  }
+
+// head_dim 64 takes up to 4 row blocks, 128 up to 2, 256 one, and two-tile
+// chunks only while nr * head_dim <= 128 (the accumulators, query and K
+// fragments stay in registers)
+#define PA_DEFINE_MQ_LAUNCHER(NAME, DT)                                             \
+  bool NAME(int D, int nr, int tiles, int nw, dim3 grid, hipStream_t s, const MQParams& p) { \
+    switch ((D * 8 + nr) * 4 + tiles) {                                             \
+      PA_MQ_CASE(DT, 64, 1, 1) PA_MQ_CASE(DT, 64, 1, 2)                             \
+      PA_MQ_CASE(DT, 64, 2, 1) PA_MQ_CASE(DT, 64, 2, 2)                             \
+      PA_MQ_CASE(DT, 64, 4, 1)                                                      \
+      PA_MQ_CASE(DT, 128, 1, 1) PA_MQ_CASE(DT, 128, 1, 2)                           \
+      PA_MQ_CASE(DT, 128, 2, 1)                                                     \
+      PA_MQ_CASE(DT, 256, 1, 1)                                                     \
       default: return false;                                                        \
     }                                                                               \
   }

@@ -122,7 +122,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
       qf[s] = c16 < G ? ld16(qb + (size_t)s * 32 * EB) : make_uint4(0, 0, 0, 0);
   }
 
-  const int32_t* bt = p.block_tables + (size_t)b * p.max_blocks_per_seq;
+  const int32_t* bt = table_row(p, b);
   const int log2_bs = p.log2_bs;
   const int last_pg = (hi - 1) >> log2_bs;
   int pg0 = -(1 << 30);

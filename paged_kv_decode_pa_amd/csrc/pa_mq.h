@@ -1,0 +1,427 @@
+// Multi-query paged attention: a sequence brings n >= 1 new tokens (a prompt
+// chunk, or a draft to verify), the last n of its L positions, and each new
+// token attends causally to the keys up to its own position.
+//
+// Two paths share one plan kernel:
+//   * per token: every query token runs as its own decode sequence (context
+//     pos + 1, its sequence's block table) through the decode kernels; any
+//     dtype and shape the decode path takes;
+//   * tiled (16-bit KV, pages of 16+ tokens): the rows of a (sequence, KV
+//     head) are the pairs (new token i, query head h of the group), numbered
+//     f = i * G + h, and a wavefront takes R = 16 * NR consecutive rows as
+//     the N side of the matrix-core tiles.  Each K/V chunk is then read once
+//     for R rows instead of once per token, and every row masks the keys
+//     past its own position.
+//
+// Tiled wavefront, per chunk of NT = 16 * TILES tokens inside one page:
+//   q.k   S^T[t][r] = K[t][:] . Q[r][:] for each 16-row block (NR of them),
+//         K fragments (A) loaded once for all blocks;
+//   mask  row r keeps keys in [its window start, its position];
+//   softmax per row, lanes c16 of a block own row c16 (4 lanes share it);
+//   P.V   O^T[d][r] += V^T[d][t] . P^T[t][r], V^T gathered from the chunk in
+//         LDS once per 16 dims for all row blocks.
+// Workgroups hold 1..8 wavefronts that take a partition's chunks
+// round-robin and merge in LDS; split-K partials use the decode layout, so
+// the decode reduce merges them (each token's context is pos + 1).
+#pragma once
+
+#include "pa_mfma.h"
+
+namespace pa {
+
+struct MQParams {
+  void* out;                  // [T, Hq, D]
+  float* tmp_out;             // [T, Hq, NP, D]
+  float* max_logits;          // [T, Hq, NP], base-2 logits
+  float* exp_sums;            // [T, Hq, NP]
+  const int2* tiles;          // (sequence, first row) of each tile
+  const int32_t* num_tiles;   // [1]
+  const void* q;              // [T, Hq, D]
+  const void* k_cache;        // [NB, bs, Hkv, D]
+  const void* v_cache;
+  const int32_t* block_tables;  // [B, max_blocks_per_seq]
+  const int32_t* context_lens;  // [B], counting every new token
+  const int32_t* query_start;   // [B + 1]
+  int max_blocks_per_seq;
+  int max_context_len;
+  int num_heads;
+  int num_kv_heads;
+  int group;                  // G = Hq / Hkv
+  int num_blocks;
+  int log2_bs;
+  int window;
+  int part;                   // partition size in tokens (> 0)
+  int num_parts;
+  int max_tiles;              // grid tiles per (KV head, partition)
+  int num_tokens;             // T
+  float qk_mul;
+  float cap_mul;
+};
+
+template <int DT, int D, int NR, int TILES>
+struct MQShape {
+  static constexpr int R = 16 * NR;             // rows per wavefront
+  static constexpr int NT = 16 * TILES;         // tokens per chunk
+  static constexpr int KS = D / 32;             // q.k k-steps
+  static constexpr int MT = D / 16;             // P.V tiles over head_dim
+  static constexpr int VBYTES = NT * D * 2;     // V chunk in LDS
+  static constexpr int VLOADS = VBYTES / 1024;  // 1 KB direct-to-LDS loads
+  // LDS floats per wavefront: the two V chunks (after the loop: the [R][D]
+  // accumulators), the block-table window, max and sum per row
+  static constexpr int BUF = (2 * VBYTES / 4 > R * D) ? 2 * VBYTES / 4 : R * D;
+  static constexpr int TBL = BUF;
+  static constexpr int ML = TBL + 64;
+  static constexpr int LDS_FLOATS = ML + 2 * R;
+  static_assert(VBYTES % 1024 == 0, "chunk must fill whole 1 KB LDS loads");
+};
+
+template <int DT, int D, int NR, int TILES>
+__global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
+  using S = MQShape<DT, D, NR, TILES>;
+  constexpr int R = S::R, NT = S::NT, KS = S::KS, MT = S::MT, VLOADS = S::VLOADS;
+  constexpr int EB = 2;
+  typedef const __attribute__((address_space(4))) int32_t cint32;
+  typedef const __attribute__((address_space(4))) uint64_t cu64;
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  const int c16 = lane & 15;
+  const int j = lane >> 4;
+
+  extern __shared__ float smem[];
+  float* s_wave = smem + w * S::LDS_FLOATS;
+  char* vbuf = reinterpret_cast<char*>(s_wave);
+  int32_t* tbl = reinterpret_cast<int32_t*>(s_wave + S::TBL);
+
+  // unit: KV head fastest, then tiles (a sequence's tiles side by side, so
+  // they share its pages in L2), then partitions
+  const int Hq = p.num_heads;
+  const int G = p.group;
+  const int g = blockIdx.x % p.num_kv_heads;
+  const int rest = blockIdx.x / p.num_kv_heads;
+  const int tile = rest % p.max_tiles;
+  const int part = rest / p.max_tiles;
+  if (tile >= *(cint32*)p.num_tiles) return;
+  const uint64_t tl = ((cu64*)p.tiles)[tile];
+  const int b = (int)(uint32_t)tl;
+  const int f0 = (int)(uint32_t)(tl >> 32);
+  // the sequence's rows, clamped to [0, T) whatever query_start holds
+  const int q0 = min(max(((cint32*)p.query_start)[b], 0), p.num_tokens);
+  const int n = min(max(((cint32*)p.query_start)[b + 1] - q0, 0), p.num_tokens - q0);
+  const int f_end = min(f0 + R, n * G);
+  const int L = min(((cint32*)p.context_lens)[b], p.max_context_len);
+  const int W = p.window;
+  const int P = p.part;
+  auto key_lo = [&](int pos) { return W > 0 ? max(0, pos + 1 - W) : 0; };
+  const int i_first = f0 / G;
+  const int i_last = (f_end - 1) / G;
+  const int lo = max(key_lo(L - n + i_first), part * P);
+  const int hi = min(L - n + i_last + 1, part * P + P);
+  if (f0 >= f_end || lo >= hi) return;
+
+  // this lane's rows (one per 16-row block): keys it attends to within the
+  // unit, and its query fragments (B operand of q.k; zero for rows past the
+  // sequence's last)
+  int a_lo[NR], a_hi[NR];
+  uint4 qf[NR][KS];
+#pragma unroll
+  for (int nb = 0; nb < NR; ++nb) {
+    const int f = f0 + 16 * nb + c16;
+    const bool act = f < f_end;
+    const int i = act ? f / G : i_first;
+    const int h = act ? f - i * G : 0;
+    const int pos = L - n + i;
+    a_lo[nb] = act ? max(lo, key_lo(pos)) : 0;
+    a_hi[nb] = act ? min(hi, pos + 1) : 0;
+    const char* qb = static_cast<const char*>(p.q) +
+                     (((size_t)(q0 + i) * Hq + (size_t)g * G + h) * D + 8 * j) * EB;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qf[nb][s] = act ? ld16(qb + (size_t)s * 32 * EB) : make_uint4(0, 0, 0, 0);
+  }
+
+  const int32_t* bt = p.block_tables + (size_t)b * p.max_blocks_per_seq;
+  const int log2_bs = p.log2_bs;
+  const int last_pg = (hi - 1) >> log2_bs;
+  int pg0 = -(1 << 30);
+  auto refill = [&](int first) {
+    pg0 = first;
+    const int pg = first + lane;
+    const int v = pg <= last_pg ? bt[pg] : 0;
+    tbl[lane] = v;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  const uint32_t row_bytes = (uint32_t)(p.num_kv_heads * D * EB);
+  const uint32_t page_bytes = row_bytes << log2_bs;
+  const uint32_t head_bytes = (uint32_t)(g * D * EB);
+  const char* kbase = static_cast<const char*>(p.k_cache);
+  const char* vbase = static_cast<const char*>(p.v_cache);
+  // prefetch target past the last chunk: the tile's first query row (the
+  // descriptor's bounds turn anything beyond it into zeros)
+  const char* dummy = static_cast<const char*>(p.q) +
+                      ((size_t)(q0 + i_first) * Hq + (size_t)g * G) * D * EB;
+
+  // V copy: instruction i moves LDS bytes [1024 i, 1024 i + 1024); lane l's
+  // 16 bytes hold row r, stored segment sg ^ f(r) of global segment sg
+  int v_row[VLOADS];
+  uint32_t v_seg_bytes[VLOADS];
+#pragma unroll
+  for (int i = 0; i < VLOADS; ++i) {
+    const int o = i * 1024 + lane * 16;
+    const int r = o / (2 * D);
+    const int sg = ((o % (2 * D)) >> 4) ^ (((r >> 2) & 3) << 1);
+    v_row[i] = r;
+    v_seg_bytes[i] = head_bytes + (uint32_t)(sg * 16);
+  }
+
+  struct Addr {
+    rsrc_t kr, vr;
+    uint32_t soff;
+    int rlo, rhi;
+  };
+  auto chunk_addr = [&](int c, Addr& a) {
+    const int cs = c * NT;
+    const int cpg = max(cs, lo) >> log2_bs;
+    if (cpg < pg0 || cpg - pg0 >= 64) refill(cpg);
+    int phys = __builtin_amdgcn_readfirstlane(tbl[cpg - pg0]);
+    phys = ((unsigned)phys < (unsigned)p.num_blocks) ? phys : 0;
+    const uint64_t base = (uint64_t)phys * page_bytes;
+    a.kr = make_rsrc(kbase + base, page_bytes);
+    a.vr = make_rsrc(vbase + base, page_bytes);
+    a.soff = (uint32_t)(cs & ((1 << log2_bs) - 1)) * row_bytes;
+    a.rlo = lo - cs;
+    a.rhi = hi - 1 - cs;
+  };
+  auto dummy_addr = [&](Addr& a) {
+    a.kr = make_rsrc(dummy, (uint32_t)(G * D * EB));
+    a.vr = a.kr;
+    a.soff = 0;
+    a.rlo = 0;
+    a.rhi = 0;
+  };
+  auto kload = [&](const Addr& a, int t, int s) -> uint4 {
+    const int r = min(max(16 * t + c16, a.rlo), a.rhi);
+    return ld16_buf(a.kr, (uint32_t)r * row_bytes + head_bytes + (uint32_t)((32 * s + 8 * j) * EB),
+                    a.soff);
+  };
+  auto vcopy = [&](const Addr& a, char* vb) {
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      const int r = min(max(v_row[i], a.rlo), a.rhi);
+      ld16_buf_to_lds(a.vr, vb + i * 1024, (uint32_t)r * row_bytes + v_seg_bytes[i], a.soff);
+    }
+  };
+
+  float m_run[NR], l_run[NR];
+  f32x4_t acc[NR][MT];
+#pragma unroll
+  for (int nb = 0; nb < NR; ++nb) {
+    m_run[nb] = kNegInf;
+    l_run[nb] = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  const int c0 = lo / NT;
+  const int c1 = (hi - 1) / NT;
+  constexpr int NK = TILES * KS;
+  constexpr int NV = VLOADS;
+  auto addr_of = [&](int cc, Addr& a) {
+    if (cc <= c1) chunk_addr(cc, a);
+    else dummy_addr(a);
+  };
+  auto issue_k = [&](const Addr& a, uint4 (&k)[TILES][KS]) {
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) k[t][s] = kload(a, t, s);
+  };
+
+  // One chunk cc, then its K slot and V buffer are refilled with chunk cn.
+  auto step = [&](int cc, int cn, uint4 (&k)[TILES][KS], char* vb) {
+    f32x4_t sc[NR][TILES];
+#pragma unroll
+    for (int nb = 0; nb < NR; ++nb)
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        sc[nb][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) sc[nb][t] = mfma_k32<DT>(k[t][s], qf[nb][s], sc[nb][t]);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    Addr an;
+    addr_of(cn, an);
+    issue_k(an, k);
+    __builtin_amdgcn_sched_barrier(0);
+
+    const int cs = cc * NT;
+    uint32_t pk[NR][2 * TILES];
+#pragma unroll
+    for (int nb = 0; nb < NR; ++nb) {
+      float pr[TILES][4];
+      if (p.cap_mul > 0.0f) {
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pr[t][i] = p.cap_mul * tanh_def(sc[nb][t][i] * p.qk_mul);
+      } else {
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pr[t][i] = sc[nb][t][i] * p.qk_mul;
+      }
+      float cmax = kNegInf;
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pos = cs + 16 * t + 4 * j + i;
+          pr[t][i] = (pos >= a_lo[nb] && pos < a_hi[nb]) ? pr[t][i] : kNegInf;
+          cmax = fmaxf(cmax, pr[t][i]);
+        }
+      cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
+      cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
+      const float m_new = fmaxf(m_run[nb], cmax);
+      // a row with no key yet keeps (-inf, 0, 0): exponents against 0
+      const float m_use = m_new == kNegInf ? 0.0f : m_new;
+      const float alpha = fast_exp2(m_run[nb] - m_use);
+      float psum = 0.0f;
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pr[t][i] = fast_exp2(pr[t][i] - m_use);
+          psum += pr[t][i];
+        }
+      l_run[nb] = l_run[nb] * alpha + psum;
+      m_run[nb] = m_new;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[nb][mt] *= alpha;
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        pk[nb][2 * t] = pack2<DT>(pr[t][0], pr[t][1]);
+        pk[nb][2 * t + 1] = pack2<DT>(pr[t][2], pr[t][3]);
+      }
+    }
+
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * NK + NV));
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int d = 16 * mt + c16;
+      uint32_t vv[2 * TILES];
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2) {
+          const int r0 = 16 * t + 4 * j + 2 * i2;
+          const uint16_t lo16 = *reinterpret_cast<const uint16_t*>(vb + v_lds_off<D>(r0, d));
+          const uint16_t hi16 = *reinterpret_cast<const uint16_t*>(vb + v_lds_off<D>(r0 + 1, d));
+          vv[2 * t + i2] = (uint32_t)lo16 | ((uint32_t)hi16 << 16);
+        }
+#pragma unroll
+      for (int nb = 0; nb < NR; ++nb) {
+        if constexpr (TILES == 2)
+          acc[nb][mt] = mfma_k32<DT>(make_uint4(vv[0], vv[1], vv[2], vv[3]),
+                                     make_uint4(pk[nb][0], pk[nb][1], pk[nb][2], pk[nb][3]),
+                                     acc[nb][mt]);
+        else
+          acc[nb][mt] = mfma_k16<DT>(make_uint2(vv[0], vv[1]), make_uint2(pk[nb][0], pk[nb][1]),
+                                     acc[nb][mt]);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    __builtin_amdgcn_sched_barrier(0);
+    vcopy(an, vb);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  uint4 kf0[TILES][KS], kf1[TILES][KS];
+  char* vb0 = vbuf;
+  char* vb1 = vbuf + S::VBYTES;
+  int c = c0 + w;
+  if (c <= c1) {
+    Addr a;
+    addr_of(c, a);
+    issue_k(a, kf0);
+    __builtin_amdgcn_sched_barrier(0);
+    vcopy(a, vb0);
+    __builtin_amdgcn_sched_barrier(0);
+    addr_of(c + nw, a);
+    issue_k(a, kf1);
+    __builtin_amdgcn_sched_barrier(0);
+    vcopy(a, vb1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma clang loop unroll(disable)
+    for (; c <= c1; c += 2 * nw) {
+      step(c, c + 2 * nw, kf0, vb0);
+      step(c + nw, c + 3 * nw, kf1, vb1);
+    }
+  }
+  // drain the trailing loads (the V buffers are reused below)
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // ---- epilogue: per-row sums over the four lanes, staged in LDS ----
+  float* s_acc = s_wave;
+  float* s_ml = s_wave + S::ML;
+#pragma unroll
+  for (int nb = 0; nb < NR; ++nb) {
+    float l = l_run[nb];
+    l += shfl_xor_f(l, 16);
+    l += shfl_xor_f(l, 32);
+    const int r = 16 * nb + c16;
+    if (j == 0) {
+      s_ml[r] = m_run[nb];
+      s_ml[R + r] = l;
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_acc[r * D + 16 * mt + 4 * j + i] = acc[nb][mt][i];
+  }
+  __syncthreads();
+
+  // merge the wavefronts and write each row: the output when the row's keys
+  // all lie in this partition, else its split-K partial
+  for (int e = threadIdx.x; e < R * D; e += blockDim.x) {
+    const int r = e / D;
+    const int d = e % D;
+    const int f = f0 + r;
+    if (f >= f_end) break;  // rows are in order: the rest are past the end
+    float M = kNegInf;
+    for (int v = 0; v < nw; ++v) M = fmaxf(M, smem[v * S::LDS_FLOATS + S::ML + r]);
+    if (M == kNegInf) continue;  // no key of this row in the partition
+    float den = 0.0f, num = 0.0f;
+    for (int v = 0; v < nw; ++v) {
+      const float* lv = smem + v * S::LDS_FLOATS;
+      const float fct = fast_exp2(lv[S::ML + r] - M);
+      den += fct * lv[S::ML + R + r];
+      num += fct * lv[r * D + d];
+    }
+    const int i = f / G;
+    const int h = f - i * G;
+    const int pos = L - n + i;
+    const size_t row = (size_t)(q0 + i) * Hq + (size_t)g * G + h;
+    if (key_lo(pos) / P == pos / P) {
+      store_elem<DT>(p.out, row * D + d, num / den);
+    } else {
+      const size_t pi = row * p.num_parts + part;
+      p.tmp_out[pi * D + d] = num / den;
+      if (d == 0) {
+        p.max_logits[pi] = M;
+        p.exp_sums[pi] = den;
+      }
+    }
+  }
+}
+
+}  // namespace pa

@@ -102,4 +102,52 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   if (t == 0) *plan.num_items = base;
 }
 
+// Plan of a multi-query launch (one workgroup of 1024 threads):
+//   vctx[tok] = context of query token tok (its position + 1, clamped to
+//   [0, max_context_len]); vrow[tok] = its sequence (per-token path);
+//   tiles = (sequence, first row) for every R rows of each sequence's
+//   n * G rows (tiled path), at most tile_cap of them.  Null outputs are
+//   skipped.
+__global__ __launch_bounds__(1024) void mq_plan_kernel(const int32_t* __restrict__ query_start,
+                                                       const int32_t* __restrict__ context_lens,
+                                                       int num_seqs, int num_tokens,
+                                                       int max_context_len, int G, int R,
+                                                       int2* tiles, int tile_cap,
+                                                       int32_t* num_tiles, int32_t* vctx,
+                                                       int32_t* vrow) {
+  __shared__ int s_tmp[17];
+  const int t = threadIdx.x;
+  if (tiles != nullptr) {
+    int base = 0;
+    for (int k0 = 0; k0 < num_seqs; k0 += blockDim.x) {
+      const int b = k0 + t;
+      int nt = 0;
+      if (b < num_seqs) {
+        // rows of the sequence's tokens that lie in [0, num_tokens)
+        const int q0 = min(max(query_start[b], 0), num_tokens);
+        const int n = min(max(query_start[b + 1] - q0, 0), num_tokens - q0);
+        nt = (n * G + R - 1) / R;
+      }
+      int total;
+      const int off = base + block_exclusive_scan(nt, s_tmp, &total);
+      for (int i = 0; i < nt && off + i < tile_cap; ++i) tiles[off + i] = make_int2(b, i * R);
+      base += total;
+    }
+    if (t == 0) *num_tiles = min(base, tile_cap);
+  }
+  for (int tok = t; tok < num_tokens; tok += blockDim.x) {
+    // the sequence that owns tok: the last b with query_start[b] <= tok
+    int lo = 0, hi = num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (query_start[mid] <= tok) lo = mid;
+      else hi = mid - 1;
+    }
+    const int n = query_start[lo + 1] - query_start[lo];
+    const int pos = context_lens[lo] - n + (tok - query_start[lo]);
+    vctx[tok] = min(max(pos + 1, 0), max_context_len);
+    if (vrow != nullptr) vrow[tok] = lo;
+  }
+}
+
 }  // namespace pa

@@ -163,6 +163,71 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, softcap=0.0, 
     return out
 
 
+def mq_partition_size(num_seqs, num_tokens, max_query_len, num_heads, num_kv_heads, head_dim,
+                      block_size, max_context_len, window=0, dtype=torch.bfloat16) -> int:
+    """The library's choice of split-K partition size for a multi-query shape."""
+    return int(_lib.load().pa_mq_partition_size(
+        num_seqs, num_tokens, max_query_len, num_heads, num_kv_heads, head_dim, block_size,
+        max_context_len, window, _DTYPE[dtype]))
+
+
+def mq_workspace_size(num_seqs, num_tokens, num_heads, num_kv_heads, head_dim, max_context_len,
+                      partition_size) -> int:
+    return int(_lib.load().pa_mq_workspace_size(num_seqs, num_tokens, num_heads, num_kv_heads,
+                                                head_dim, max_context_len, partition_size))
+
+
+def mq_attention(q, query_start, k_cache, v_cache, block_tables, context_lens, scale, softcap=0.0,
+                 window=0, partition_size=None, max_context_len=None, max_query_len=None,
+                 out=None, workspace=None):
+    """Multi-query paged attention (pa_mq_attention): sequence b's new tokens
+    are q's rows query_start[b] .. query_start[b+1]-1, the last n_b of its
+    context_lens[b] positions, each attending causally to the keys up to its
+    own position.
+
+    q [T, Hq, D]; query_start int32 [B+1]; context_lens int32 [B] (counting
+    the new tokens, whose K/V rows are already in the cache).
+    ``max_context_len`` / ``max_query_len`` default to the maxima of the
+    device arrays (one device sync each)."""
+    _dev(q, query_start, k_cache, v_cache, block_tables, context_lens, out)
+    T, Hq, D = q.shape
+    NB, bs, Hkv, D2 = k_cache.shape
+    B = context_lens.shape[0]
+    if D2 != D:
+        raise ValueError("head_dim of q and caches differ")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be int32 [num_seqs, max_blocks_per_seq]")
+    if context_lens.dtype != torch.int32 or context_lens.dim() != 1:
+        raise ValueError("context_lens must be int32 [num_seqs]")
+    if query_start.dtype != torch.int32 or tuple(query_start.shape) != (B + 1,):
+        raise ValueError("query_start must be int32 [num_seqs + 1]")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q and caches must share a dtype")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if B else 0
+    if max_query_len is None:
+        max_query_len = int((query_start[1:] - query_start[:-1]).max().item()) if B else 0
+    max_query_len = max(1, min(int(max_query_len), T)) if T else 0
+    if partition_size is None:
+        partition_size = mq_partition_size(B, T, max(max_query_len, 1), Hq, Hkv, D, bs,
+                                           max_context_len, window, q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.dtype != q.dtype or tuple(out.shape) != (T, Hq, D):
+        raise ValueError("out must match q")
+    if workspace is None:
+        n = mq_workspace_size(B, T, Hq, Hkv, D, max_context_len, partition_size)
+        workspace = torch.empty((n + 3) // 4, dtype=torch.float32, device=q.device) if n else None
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _lib.check("pa_mq_attention", _lib.load().pa_mq_attention(
+        out.data_ptr(), ws_ptr, ws_bytes, q.data_ptr(), query_start.data_ptr(), T,
+        int(max_query_len), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+        block_tables.shape[1], context_lens.data_ptr(), int(max_context_len), B, Hq, Hkv, D, bs,
+        NB, float(scale), float(softcap), int(window), int(partition_size), _dt(q), _stream()))
+    return out
+
+
 class Step:
     """One layer-step over fixed buffers: reshape_and_cache of the new rows
     (if given), pa_decode and pa_decode_reduce, run through pa_step, or

@@ -170,3 +170,61 @@ def test_step_graph_argument_checks():
     assert lib.pa_step_graph_create(None, None, ctypes.byref(h)) == -1
     assert lib.pa_step_graph_launch(None, None) == -1
     assert lib.pa_step_graph_destroy(None) == 0
+
+
+# --------------------------------------------------------------------------
+# multi-query attention
+# --------------------------------------------------------------------------
+def mq_args(**over):
+    a = dict(out=FAKE, ws=None, ws_bytes=0, q=FAKE, qs=FAKE, T=12, maxq=6, kc=FAKE, vc=FAKE,
+             bt=FAKE, maxb=8, cl=FAKE, maxL=128, B=2, Hq=8, Hkv=2, D=64, bs=16, NB=64,
+             scale=0.125, softcap=0.0, window=0, P=0, dt=_lib.PA_BF16, stream=None)
+    a.update(over)
+    return a
+
+
+def call_mq(a):
+    return _lib.load().pa_mq_attention(
+        a["out"], a["ws"], a["ws_bytes"], a["q"], a["qs"], a["T"], a["maxq"], a["kc"], a["vc"],
+        a["bt"], a["maxb"], a["cl"], a["maxL"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+        a["NB"], a["scale"], a["softcap"], a["window"], a["P"], a["dt"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(out=None), -1),
+    (dict(qs=None), -1),
+    (dict(cl=None), -1),
+    (dict(B=0), -1),                      # tokens but no sequences
+    (dict(maxq=0), -1),
+    (dict(maxq=13), -1),                  # more than num_tokens
+    (dict(T=-1), -1),
+    (dict(Hq=6, Hkv=4), -1),
+    (dict(maxL=129), -1),
+    (dict(P=24), -1),
+    (dict(softcap=-2.0), -1),
+    (dict(D=80), -2),
+    (dict(bs=24), -2),
+    (dict(dt=_lib.PA_F32, Hq=6, Hkv=2), -2),   # per-token path: group of 3 not built
+    (dict(), -3),                         # no workspace
+    (dict(ws=FAKE, ws_bytes=64), -3),
+])
+def test_mq_rejects_bad_arguments(over, status):
+    assert call_mq(mq_args(**over)) == status
+
+
+def test_mq_with_no_tokens_is_a_noop():
+    assert call_mq(mq_args(T=0, maxq=0, out=None, q=None)) == 0
+
+
+def test_mq_workspace_covers_the_decode_workspace_of_every_token():
+    for B, T, L, P in ((4, 40, 300, 64), (512, 2560, 1024, 0), (1, 4096, 4096, 512)):
+        assert (pa.mq_workspace_size(B, T, 8, 2, 128, L, P)
+                >= pa.workspace_size(T, 8, 128, L, P) + 2 * T * 4)
+    assert pa.mq_workspace_size(3, 0, 8, 2, 128, 300, 64) == 0
+
+
+def test_mq_partition_choice_is_a_multiple_of_block_size():
+    for bs in (1, 16, 32):
+        for B, T, q, L in ((512, 2560, 5, 1024), (64, 575, 512, 4096), (4, 8192, 2048, 2048)):
+            P = pa.mq_partition_size(B, T, q, 8, 4, 256, bs, L)
+            assert P >= 0 and P % bs == 0

@@ -1,0 +1,215 @@
+"""Multi-query paged attention on the GPU (pa_mq_attention) against the
+oracle: each new token attends causally to the keys up to its own position.
+
+Both paths are covered: the tiled matrix-core path (f16/bf16, pages of 16+
+tokens, any group size) and the per-token path (every other shape, or
+PA_MQ_TILED=0).  New tokens' K/V rows land through pa_reshape_and_cache
+first, into slots the generator poisoned."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import oracle as O
+from workloads import make_mq_case, mq_workload
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "f16": 2e-2, "bf16": 2e-2}
+
+
+class DeviceMQ:
+    def __init__(self, c):
+        import torch
+        from gpu_util import upload
+        self.c = c
+        self.q = upload(c.q, c.dtype)
+        self.k_cache = upload(c.k_cache, c.dtype)
+        self.v_cache = upload(c.v_cache, c.dtype)
+        self.block_tables = torch.from_numpy(c.block_tables).cuda()
+        self.context_lens = torch.from_numpy(c.context_lens).cuda()
+        self.query_start = torch.from_numpy(c.query_start).cuda()
+        self.key = self.value = self.slots = None
+        if c.slot_mapping is not None:
+            self.key = upload(c.key, c.dtype)
+            self.value = upload(c.value, c.dtype)
+            self.slots = torch.from_numpy(c.slot_mapping).cuda()
+
+    def run(self, partition_size=None, tiled=None, out=None, max_query_len=None):
+        import torch
+        import paged_kv_decode_pa_amd as pa
+        c = self.c
+        if tiled is not None:
+            os.environ["PA_MQ_TILED"] = "1" if tiled else "0"
+        try:
+            if self.slots is not None:
+                pa.reshape_and_cache(self.key, self.value, self.k_cache, self.v_cache, self.slots)
+            P = c.partition_size if partition_size is None else partition_size
+            out = pa.mq_attention(self.q, self.query_start, self.k_cache, self.v_cache,
+                                  self.block_tables, self.context_lens, c.scale, c.softcap,
+                                  c.window, partition_size=P, max_context_len=c.max_context_len,
+                                  max_query_len=max_query_len or max(1, c.max_query_len), out=out)
+            torch.cuda.synchronize()
+        finally:
+            os.environ.pop("PA_MQ_TILED", None)
+        return out
+
+
+def check(got_t, want, dtype, rows=None):
+    from gpu_util import to_f64
+    got = to_f64(got_t)
+    if rows is not None:
+        got = got[rows]
+    assert np.isfinite(got).all(), "non-finite output"
+    err = np.abs(got - want).max() if got.size else 0.0
+    assert err <= TOL[dtype], f"max abs error {err:.3g} > {TOL[dtype]}"
+    return err
+
+
+# (dtype, G, D, bs, softcap, window, partition, context lens, query lens)
+SHAPES = [
+    ("bf16", 2, 256, 16, 50.0, 0, 0, [40, 77, 5, 130], [5, 77, 1, 9]),
+    ("bf16", 2, 256, 16, 50.0, 0, 32, [40, 77, 5, 130], [5, 77, 1, 9]),
+    ("f16", 8, 64, 32, 0.0, 0, 0, [300, 64, 33], [17, 64, 2]),
+    ("f16", 8, 64, 32, 0.0, 0, 64, [300, 64, 33], [17, 64, 2]),
+    ("bf16", 4, 128, 32, 30.0, 45, 0, [200, 97, 160], [33, 97, 6]),
+    ("bf16", 4, 128, 16, 0.0, 20, 48, [200, 97, 160], [33, 50, 6]),
+    ("f16", 1, 128, 64, 0.0, 0, 128, [250, 129], [70, 129]),
+    ("bf16", 16, 64, 16, 20.0, 0, 0, [90, 31, 46], [3, 31, 5]),
+    ("bf16", 3, 64, 16, 0.0, 0, 32, [70, 48], [11, 48]),     # group of 3 heads
+    ("f16", 2, 64, 16, 0.0, 7, 16, [61, 18, 9], [13, 18, 9]),
+]
+
+
+def _id(s):
+    return f"{s[0]}-g{s[1]}-d{s[2]}-bs{s[3]}-c{int(s[4])}-w{s[5]}-p{s[6]}"
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[_id(s) for s in SHAPES])
+@pytest.mark.parametrize("tiled", [True, False], ids=["tiled", "pertoken"])
+def test_mq_shapes(shape, tiled):
+    from gpu_util import say
+    dtype, G, D, bs, cap, W, P, L, n = shape
+    if not tiled and G not in (1, 2, 4, 8, 16):
+        pytest.skip("the per-token path takes the decode group sizes")
+    say(f"mq {_id(shape)} tiled={tiled}")
+    Hkv = 2
+    c = make_mq_case(Hq=G * Hkv, Hkv=Hkv, D=D, bs=bs, dtype=dtype, context_lens=L, query_lens=n,
+                     softcap=cap, window=W, partition_size=P, seed=D + G + bs + W,
+                     new_rows=True)
+    got = DeviceMQ(c).run(tiled=tiled)
+    check(got, oracle.multi_query_case(c), dtype)
+
+
+@pytest.mark.parametrize("dtype,bs", [("f32", 16), ("f32", 1), ("bf16", 8), ("f16", 1)])
+def test_mq_per_token_only_shapes(dtype, bs):
+    """f32 and pages under 16 tokens always run per token."""
+    from gpu_util import say
+    say(f"mq per-token {dtype} bs={bs}")
+    c = make_mq_case(Hq=8, Hkv=2, D=64, bs=bs, dtype=dtype, context_lens=[45, 100, 17],
+                     query_lens=[9, 100, 3], softcap=10.0, partition_size=32 if bs <= 32 else 0,
+                     seed=5 + bs, new_rows=True)
+    got = DeviceMQ(c).run()
+    check(got, oracle.multi_query_case(c), dtype)
+
+
+def test_mq_one_token_matches_decode_bitwise():
+    """With one new token per sequence the per-token path runs the decode
+    kernels on the same units: bit-identical to pa_decode."""
+    import torch
+    import paged_kv_decode_pa_amd as pa
+    from gpu_util import say
+    say("mq one token vs decode")
+    L = [33, 500, 1, 257, 64]
+    c = make_mq_case(Hq=8, Hkv=4, D=256, bs=16, dtype="bf16", context_lens=L,
+                     query_lens=[1] * len(L), softcap=50.0, partition_size=128, seed=9)
+    d = DeviceMQ(c)
+    got = d.run()
+    dec = pa.decode(d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, c.scale,
+                    c.softcap, c.window, partition_size=128, max_context_len=c.max_context_len)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), dec.view(torch.int16))
+
+
+def test_mq_empty_sequences_and_no_tokens():
+    import torch
+    import paged_kv_decode_pa_amd as pa
+    from gpu_util import say
+    say("mq empty sequences")
+    c = make_mq_case(Hq=4, Hkv=2, D=64, bs=16, dtype="bf16", context_lens=[20, 0, 35, 9],
+                     query_lens=[4, 0, 0, 9], partition_size=16, seed=2, new_rows=True)
+    for tiled in (True, False):
+        check(DeviceMQ(c).run(tiled=tiled), oracle.multi_query_case(c), "bf16")
+    z = make_mq_case(Hq=4, Hkv=2, D=64, bs=16, dtype="bf16", context_lens=[20, 7],
+                     query_lens=[0, 0], seed=3)
+    out = DeviceMQ(z).run()
+    assert out.shape == (0, 4, 64)
+
+
+def test_mq_chunked_prefill_matches_whole_prompt():
+    """A 300-token prompt prefilled in chunks of 128 (each chunk attending to
+    the cache so far plus itself) gives the rows of one whole-prompt
+    prefill."""
+    import torch
+    import paged_kv_decode_pa_amd as pa
+    from gpu_util import say, to_f64, upload
+    say("mq chunked prefill")
+    Lp = 300
+    whole = make_mq_case(Hq=8, Hkv=4, D=128, bs=32, dtype="f16", context_lens=[Lp],
+                         query_lens=[Lp], seed=11, new_rows=True)
+    ref = to_f64(DeviceMQ(whole).run())
+    d = DeviceMQ(whole)
+    pa.reshape_and_cache(d.key, d.value, d.k_cache, d.v_cache, d.slots)
+    rows = []
+    for a in range(0, Lp, 128):
+        e = min(Lp, a + 128)
+        qs = torch.tensor([0, e - a], dtype=torch.int32, device="cuda")
+        cl = torch.tensor([e], dtype=torch.int32, device="cuda")
+        o = pa.mq_attention(d.q[a:e].contiguous(), qs, d.k_cache, d.v_cache, d.block_tables, cl,
+                            whole.scale, 0.0, 0, partition_size=64, max_context_len=e,
+                            max_query_len=e - a)
+        rows.append(to_f64(o))
+    got = np.concatenate(rows)
+    assert np.abs(got - ref).max() <= 2e-2
+    np.testing.assert_allclose(ref, oracle.multi_query_case(whole), rtol=0, atol=2e-2)
+
+
+def test_mq_output_guard_band_untouched():
+    import torch
+    from gpu_util import say
+    say("mq guard band")
+    c = make_mq_case(Hq=8, Hkv=2, D=128, bs=16, dtype="bf16", context_lens=[50, 70],
+                     query_lens=[7, 30], partition_size=32, seed=4, new_rows=True)
+    d = DeviceMQ(c)
+    big = torch.full((c.T + 3, 8, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    d.run(out=big[:c.T])
+    assert torch.all(big[c.T:] == 7.0)
+    check(big[:c.T], oracle.multi_query_case(c), "bf16")
+
+
+def _sampled(c, k, seed):
+    """Oracle rows for k sampled tokens (each computed on its own)."""
+    kc, vc = O.reshape_and_cache(c.key, c.value, c.k_cache, c.v_cache, c.slot_mapping)
+    rng = np.random.default_rng(seed)
+    toks = np.sort(rng.choice(c.T, size=min(k, c.T), replace=False))
+    # always the first and last token of the longest sequence
+    b = int(np.argmax(c.query_lens))
+    toks = np.unique(np.concatenate([toks, [c.query_start[b], c.query_start[b + 1] - 1]]))
+    want = []
+    for t in toks:
+        b = int(np.searchsorted(c.query_start, t, side="right") - 1)
+        pos = int(c.context_lens[b]) - int(c.query_lens[b]) + int(t - c.query_start[b])
+        want.append(O.attend(c.q[t], kc, vc, c.block_tables, b, pos + 1, c.scale, c.softcap,
+                             c.window, c.dtype))
+    return toks, np.stack(want)
+
+
+@pytest.mark.parametrize("name", ["spec5", "chunk512", "prefill"])
+def test_mq_workloads_sampled(name):
+    from gpu_util import say
+    say(f"mq workload {name}")
+    c = mq_workload(name)
+    got = DeviceMQ(c).run()
+    toks, want = _sampled(c, 48, 7)
+    check(got, want, c.dtype, rows=toks)
