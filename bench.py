@@ -108,12 +108,185 @@ def cpu_baseline(case, budget_s: float):
                       f"{passes} pass(es) in {dt:.1f} s"}
 
 
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}
+
+
+def cpu_baseline_mq(case, budget_s: float):
+    """The oracle on a multi-query workload: the new rows land, then the
+    query tokens are attended one by one in order until `budget_s` seconds
+    have been spent."""
+    import oracle
+    from oracle import oracle as O
+    eb = 2 if case.dtype != "f32" else 4
+    t0 = time.perf_counter()
+    kc, vc = oracle.reshape_and_cache(case.key, case.value, case.k_cache, case.v_cache,
+                                      case.slot_mapping)
+    toks = flops = 0
+    L = case.context_lens.astype(np.int64)
+    done = False
+    for b in range(case.B):
+        n = int(case.query_lens[b])
+        for i in range(n):
+            pos = int(L[b]) - n + i
+            O.attend(case.q[case.query_start[b] + i], kc, vc, case.block_tables, b, pos + 1,
+                     case.scale, case.softcap, case.window, case.dtype)
+            keys = pos + 1 if case.window <= 0 else min(pos + 1, case.window)
+            flops += 4 * case.D * case.Hq * keys
+            toks += 1
+            if time.perf_counter() - t0 >= budget_s:
+                done = True
+                break
+        if done:
+            break
+    dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "tokens_per_s": round(toks / dt, 2),
+            "sample": f"float64 numpy oracle on this workload: reshape_and_cache of its "
+                      f"{case.T} new rows, then {toks} of its {case.T} query tokens in order "
+                      f"in {dt:.1f} s"}
+
+
+def bench_mq(args):
+    """Multi-query step: reshape_and_cache of every new token's K/V row, then
+    pa_mq_attention (plan, attention and, when split, the reduce)."""
+    import torch
+    import paged_kv_decode_pa_amd as pa
+    from workloads import MQ_WORKLOADS, mq_workload
+
+    dev = torch.device("cuda:0")
+    print(f"[bench] building workload {args.workload} ({MQ_WORKLOADS[args.workload]})",
+          file=sys.stderr, flush=True)
+    case = mq_workload(args.workload, partition_size=args.partition_size)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[case.dtype]
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(tdt)
+        return torch.from_numpy(a).to(dev)
+
+    q, kc, vc = up(case.q), up(case.k_cache), up(case.v_cache)
+    bt = torch.from_numpy(case.block_tables).to(dev)
+    cl = torch.from_numpy(case.context_lens).to(dev)
+    qs = torch.from_numpy(case.query_start).to(dev)
+    key, value = up(case.key), up(case.value)
+    slots = torch.from_numpy(case.slot_mapping).to(dev)
+    T, Hq, D = case.q.shape
+    maxL, maxq = case.max_context_len, case.max_query_len
+    P = case.partition_size
+    if P is None:
+        P = pa.mq_partition_size(case.B, T, maxq, Hq, case.Hkv, D, case.bs, maxL, case.window,
+                                 tdt)
+    out = torch.empty_like(q)
+    n = pa.mq_workspace_size(case.B, T, Hq, case.Hkv, D, maxL, P)
+    ws = torch.empty((n + 3) // 4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def step(record=False):
+        pa.reshape_and_cache(key, value, kc, vc, slots)
+        if record:
+            e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            e[0].record(stream)
+        pa.mq_attention(q, qs, kc, vc, bt, cl, case.scale, case.softcap, case.window,
+                        partition_size=P, max_context_len=maxL, max_query_len=maxq, out=out,
+                        workspace=ws)
+        if record:
+            e[1].record(stream)
+            ev.append(e)
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(record=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    attn_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    print(f"[bench] timed {args.steps} steps: {ms_step*1e3:.1f} us/step wall, "
+          f"pa_mq_attention {attn_ms*1e3:.1f} us (HIP events)", file=sys.stderr, flush=True)
+
+    max_err = None
+    if not args.no_check:
+        from oracle import oracle as O
+        kc0, vc0 = O.reshape_and_cache(case.key, case.value, case.k_cache, case.v_cache,
+                                       case.slot_mapping)
+        b = int(np.argmax(case.context_lens))
+        toks = sorted({0, T - 1, int(case.query_start[b]), int(case.query_start[b + 1]) - 1})
+        got = out.float().cpu().numpy().astype(np.float64)
+        max_err = 0.0
+        for t in toks:
+            bb = int(np.searchsorted(case.query_start, t, side="right") - 1)
+            pos = int(case.context_lens[bb]) - int(case.query_lens[bb]) + t - int(case.query_start[bb])
+            want = O.attend(case.q[t], kc0, vc0, case.block_tables, bb, pos + 1, case.scale,
+                            case.softcap, case.window, case.dtype)
+            max_err = max(max_err, float(np.abs(got[t] - want).max()))
+        print(f"[bench] parity spot-check on tokens {toks}: max abs err {max_err:.3e}",
+              file=sys.stderr, flush=True)
+        if not (max_err <= 2e-2):
+            print("[bench] PARITY FAILURE", file=sys.stderr)
+            sys.exit(1)
+
+    ab = case.algorithmic_bytes()
+    flops = case.flops()
+    step_s = ms_step / 1e3
+    value = ab["total"] / step_s / 1e9
+    intensity = flops / ab["attn"]
+    ridge = MFMA_PEAK_TFLOPS[case.dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if intensity > ridge:
+        achieved = flops / (attn_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2),
+                "peak": MFMA_PEAK_TFLOPS[case.dtype], "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_PEAK_TFLOPS[case.dtype], 4)}
+    else:
+        achieved = ab["attn"] / (attn_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof.update({"traffic": None, "kernel": "pa_mq_attention (plan + attention + reduce)",
+                 "algorithmic_bytes_per_launch": ab["attn"], "flops_per_launch": flops,
+                 "flop_per_byte": round(intensity, 2), "kernel_sources": kernel_source_digest()})
+    cpu = None
+    if args.cpu_budget > 0:
+        print(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s)", file=sys.stderr,
+              flush=True)
+        cpu = cpu_baseline_mq(case, args.cpu_budget)
+    res = {
+        "metric": "multi-query paged attention: achieved HBM GB/s of the step",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": case.dtype, "data": "synthetic",
+        "config": {
+            "workload": case.name, "num_seqs": case.B, "num_tokens": T, "num_heads": Hq,
+            "num_kv_heads": case.Hkv, "head_dim": D, "block_size": case.bs,
+            "num_blocks": case.NB, "softcap": case.softcap, "window": case.window,
+            "max_context_len": maxL, "max_query_len": maxq, "partition_size": P,
+            "parallelism": "single GPU",
+        },
+        "tokens_per_s": round(T / step_s, 1),
+        "tflops": round(flops / step_s / 1e12, 2),
+        "us_per_layer_step": round(ms_step * 1e3, 2),
+        "pa_mq_attention_us": round(attn_ms * 1e3, 2),
+        "algorithmic_bytes_per_step": ab["total"],
+        "max_abs_err_vs_oracle": max_err,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", default="4",
+                    choices=["1", "2", "3", "4", "5", "spec5", "chunk512", "prefill"],
+                    help="decode workload 1-5, or a multi-query workload")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="tokens per split-K partition (0 = none); default: library's choice")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
@@ -135,6 +308,9 @@ def main():
     from workloads import WORKLOADS, workload
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if not args.workload.isdigit():
+        return bench_mq(args)
+    args.workload = int(args.workload)
     dev = torch.device("cuda:0")
     print(f"[bench] building workload {args.workload} ({WORKLOADS[args.workload]})", file=sys.stderr, flush=True)
     case = workload(args.workload, partition_size=args.partition_size)

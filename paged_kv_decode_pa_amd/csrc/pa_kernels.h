@@ -171,11 +171,11 @@ __device__ __forceinline__ void for_units(const DecodeParams& p, Body&& body) {
 // Merges the wavefronts' running (max, sum, accumulators) and writes the
 // unit's G output rows, or its split-K partials.  Wavefront v's record
 // starts at smem + v * stride: maxima at +ml, sums at +ml + G, accumulators
-// [G][D] at +acc.
+// [G][row_stride] at +acc.
 template <int DT, int D, int G>
 __device__ __forceinline__ void merge_store(const DecodeParams& p, const Unit& u,
                                             const float* smem, int stride, int ml, int acc,
-                                            int nw) {
+                                            int nw, int row_stride = D) {
   for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
     const int h = i / D;
     const int d = i % D;
@@ -186,7 +186,7 @@ __device__ __forceinline__ void merge_store(const DecodeParams& p, const Unit& u
       const float* lv = smem + v * stride;
       const float f = fast_exp2(lv[ml + h] - M);
       den += f * lv[ml + G + h];
-      num += f * lv[acc + h * D + d];
+      num += f * lv[acc + h * row_stride + d];
     }
     const size_t hq = (size_t)u.g * G + h;
     if (u.single) {

@@ -15,11 +15,12 @@
 //           K = the chunk's tokens).  B = the lane's own probabilities, in
 //           the token order the q.k result left them (any common order of
 //           the K index is valid); A = V transposed, gathered from LDS.
+//   The accumulators are rescaled only in chunks where some head's running
+//   maximum moved.
 //   Two chunks are in flight per wavefront: K in two register slots, V in
 //   two LDS buffers.  V is copied HBM -> LDS by the buffer unit (direct-to-LDS 16-byte loads,
 //   no registers in between).  Within a row the 16-byte segments are stored
-//   XOR-swizzled by (row/4) mod 4, so the four lane groups of a transposed
-//   read hit distinct LDS banks.
+//   XOR-swizzled (v_swz), so a transposed read hits distinct LDS banks.
 #pragma once
 
 #include "pa_kernels.h"
@@ -79,17 +80,50 @@ struct MfmaShape {
   static constexpr int TBL = V_F;
   static constexpr int ML = TBL + 64;
   static constexpr int ACC = ML + 2 * G;
-  static constexpr int LDS_FLOATS = ACC + G * D;
+  static constexpr int LDS_FLOATS = ACC + G * (D + 4);
   static_assert(G == 8 || G == 16, "MFMA path: 8 or 16 query heads per KV head");
   static_assert(VBYTES % 1024 == 0, "chunk must fill whole 1 KB LDS loads");
 };
 
-// byte offset of (row r, element d) of a V chunk in LDS
+// byte offset of (row r, element d) of a V chunk in LDS: 16-byte segments
+// XOR-swizzled by (r / 4) mod 4, so the four lane groups of a transposed
+// gather hit distinct LDS banks
+template <int D>
+__device__ __forceinline__ int v_swz(int r) { return ((r >> 2) & 3) << 1; }
+
 template <int D>
 __device__ __forceinline__ uint32_t v_lds_off(int r, int d) {
-  const int f = ((r >> 2) & 3) << 1;
-  return (uint32_t)(r * 2 * D + ((((d >> 3) ^ f)) << 4) + ((d & 7) << 1));
+  return (uint32_t)(r * 2 * D + (((d >> 3) ^ v_swz<D>(r)) << 4) + ((d & 7) << 1));
 }
+
+// A operand of P.V for head-dim tile mt: lane (c16, j) gets V[16t + 4j +
+// i][16mt + c16], i < 4, for each 16-token tile t, as 4 packed 16-bit values
+// per tile, gathered from the chunk in LDS.
+template <int D, int TILES>
+__device__ __forceinline__ void vt_frag(const char* vb, int mt, int c16, int j,
+                                        uint32_t (&vv)[2 * TILES]) {
+  const int d = 16 * mt + c16;
+#pragma unroll
+  for (int t = 0; t < TILES; ++t)
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2) {
+      const int r0 = 16 * t + 4 * j + 2 * i2;
+      const uint16_t lo16 = *reinterpret_cast<const uint16_t*>(vb + v_lds_off<D>(r0, d));
+      const uint16_t hi16 = *reinterpret_cast<const uint16_t*>(vb + v_lds_off<D>(r0 + 1, d));
+      vv[2 * t + i2] = (uint32_t)lo16 | ((uint32_t)hi16 << 16);
+    }
+}
+
+// true when any lane's alpha is below 1 (its running max moved): only then
+// do the accumulators need rescaling
+__device__ __forceinline__ bool any_rescale(float alpha) {
+  return __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0;
+}
+
+// Accumulators are staged in LDS as rows of D + 4 floats: 16-byte stores of
+// 16 consecutive rows then fall in distinct bank groups.
+template <int D>
+constexpr int acc_stride() { return D + 4; }
 
 template <int DT, int D, int G, int TILES, bool LOOP>
 __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParams p) {
@@ -152,7 +186,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
   for (int i = 0; i < VLOADS; ++i) {
     const int o = i * 1024 + lane * 16;
     const int r = o / (2 * D);
-    const int sg = ((o % (2 * D)) >> 4) ^ (((r >> 2) & 3) << 1);
+    const int sg = ((o % (2 * D)) >> 4) ^ v_swz<D>(r);
     v_row[i] = r;
     v_seg_bytes[i] = head_bytes + (uint32_t)(sg * 16);
   }
@@ -272,8 +306,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
       }
     l_run = l_run * alpha + psum;
     m_run = m_new;
+    if (any_rescale(alpha)) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+      for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+    }
 
     // P^T fragment: this lane's probabilities in (tile, i) order
     uint32_t pk[2 * TILES];
@@ -290,17 +326,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int d = 16 * mt + c16;
       uint32_t vv[2 * TILES];
-#pragma unroll
-      for (int t = 0; t < TILES; ++t)
-#pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2) {
-          const int r0 = 16 * t + 4 * j + 2 * i2;
-          const uint16_t lo16 = *reinterpret_cast<const uint16_t*>(vb + v_lds_off<D>(r0, d));
-          const uint16_t hi16 = *reinterpret_cast<const uint16_t*>(vb + v_lds_off<D>(r0 + 1, d));
-          vv[2 * t + i2] = (uint32_t)lo16 | ((uint32_t)hi16 << 16);
-        }
+      vt_frag<D, TILES>(vb, mt, c16, j, vv);
       if constexpr (TILES == 2)
         acc[mt] = mfma_k32<DT>(make_uint4(vv[0], vv[1], vv[2], vv[3]),
                                make_uint4(pk[0], pk[1], pk[2], pk[3]), acc[mt]);
@@ -353,11 +380,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_wave[S::ACC + c16 * D + 16 * mt + 4 * j + i] = acc[mt][i];
+      *reinterpret_cast<f32x4_t*>(s_wave + S::ACC + c16 * acc_stride<D>() + 16 * mt + 4 * j) =
+          acc[mt];
   }
   __syncthreads();
-  merge_store<DT, D, G>(p, u, smem, S::LDS_FLOATS, S::ML, S::ACC, nw);
+  merge_store<DT, D, G>(p, u, smem, S::LDS_FLOATS, S::ML, S::ACC, nw, acc_stride<D>());
   });
 }
 

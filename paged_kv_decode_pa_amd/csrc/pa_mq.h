@@ -67,8 +67,9 @@ struct MQShape {
   static constexpr int VBYTES = NT * D * 2;     // V chunk in LDS
   static constexpr int VLOADS = VBYTES / 1024;  // 1 KB direct-to-LDS loads
   // LDS floats per wavefront: the two V chunks (after the loop: the [R][D]
-  // accumulators), the block-table window, max and sum per row
-  static constexpr int BUF = (2 * VBYTES / 4 > R * D) ? 2 * VBYTES / 4 : R * D;
+  // accumulators, rows padded to D + 4), the block-table window, max and sum
+  // per row
+  static constexpr int BUF = (2 * VBYTES / 4 > R * (D + 4)) ? 2 * VBYTES / 4 : R * (D + 4);
   static constexpr int TBL = BUF;
   static constexpr int ML = TBL + 64;
   static constexpr int LDS_FLOATS = ML + 2 * R;
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
   for (int i = 0; i < VLOADS; ++i) {
     const int o = i * 1024 + lane * 16;
     const int r = o / (2 * D);
-    const int sg = ((o % (2 * D)) >> 4) ^ (((r >> 2) & 3) << 1);
+    const int sg = ((o % (2 * D)) >> 4) ^ v_swz<D>(r);
     v_row[i] = r;
     v_seg_bytes[i] = head_bytes + (uint32_t)(sg * 16);
   }
@@ -299,8 +300,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
         }
       l_run[nb] = l_run[nb] * alpha + psum;
       m_run[nb] = m_new;
+      if (any_rescale(alpha)) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[nb][mt] *= alpha;
+        for (int mt = 0; mt < MT; ++mt) acc[nb][mt] *= alpha;
+      }
 #pragma unroll
       for (int t = 0; t < TILES; ++t) {
         pk[nb][2 * t] = pack2<DT>(pr[t][0], pr[t][1]);
@@ -312,17 +315,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int d = 16 * mt + c16;
       uint32_t vv[2 * TILES];
-#pragma unroll
-      for (int t = 0; t < TILES; ++t)
-#pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2) {
-          const int r0 = 16 * t + 4 * j + 2 * i2;
-          const uint16_t lo16 = *reinterpret_cast<const uint16_t*>(vb + v_lds_off<D>(r0, d));
-          const uint16_t hi16 = *reinterpret_cast<const uint16_t*>(vb + v_lds_off<D>(r0 + 1, d));
-          vv[2 * t + i2] = (uint32_t)lo16 | ((uint32_t)hi16 << 16);
-        }
+      vt_frag<D, TILES>(vb, mt, c16, j, vv);
 #pragma unroll
       for (int nb = 0; nb < NR; ++nb) {
         if constexpr (TILES == 2)
@@ -385,8 +379,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_acc[r * D + 16 * mt + 4 * j + i] = acc[nb][mt][i];
+      *reinterpret_cast<f32x4_t*>(s_acc + r * acc_stride<D>() + 16 * mt + 4 * j) = acc[nb][mt];
   }
   __syncthreads();
 
@@ -405,7 +398,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
       const float* lv = smem + v * S::LDS_FLOATS;
       const float fct = fast_exp2(lv[S::ML + r] - M);
       den += fct * lv[S::ML + R + r];
-      num += fct * lv[r * D + d];
+      num += fct * lv[r * acc_stride<D>() + d];
     }
     const int i = f / G;
     const int h = f - i * G;
