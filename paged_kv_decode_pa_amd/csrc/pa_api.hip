@@ -254,8 +254,19 @@ static int decode_impl(void* out, void* workspace, size_t workspace_bytes, const
   const long resident = (long)kNumCUs * 16 / nw;
   const bool loop = blocks > 2 * resident && np >= 8;
   if (!loop) plan.items = nullptr;
-  pa::plan_kernel<<<dim3(1), dim3(1024), 0, s>>>(context_lens, num_seqs, max_context_len, window,
-                                                p.part, plan);
+  // The longest-first order pays for its launch only over many sequences of
+  // mixed length (measured: it gains 5% at 512 sequences and 4% at 64, and
+  // costs 30% at 4 and 6% at 16); below 48 sequences the grid runs in input
+  // order.  A looping launch always needs the plan's item list.
+  // PA_DECODE_PLAN=0/1 overrides.
+  const int plan_env = env_int("PA_DECODE_PLAN", -1);
+  const bool need_plan = loop || (plan_env >= 0 ? plan_env != 0 : num_seqs >= 48);
+  if (need_plan) {
+    pa::plan_kernel<<<dim3(1), dim3(1024), 0, s>>>(context_lens, num_seqs, max_context_len,
+                                                  window, p.part, plan);
+  } else {
+    p.order = nullptr;
+  }
   const dim3 grid((unsigned)(loop ? 2 * resident : blocks)), block(64 * nw);
   // chunks of nt tokens stay inside one page when block_size >= nt
   const bool paged = block_size >= nt;
@@ -381,7 +392,10 @@ int pa_mq_partition_size(int num_seqs, int num_tokens, int max_query_len, int nu
   const int G = num_heads / num_kv_heads;
   long units;
   if (mq_tiled(dtype, block_size, max_query_len)) {
-    const int R = 16 * mq_row_blocks(head_dim, G, max_query_len);
+    int nr = mq_row_blocks(head_dim, G, max_query_len);
+    const bool wg = (long)max_query_len * G > 16L * nr;
+    if (wg) nr = head_dim == 64 ? (nr < 2 ? nr : 2) : 1;
+    const int R = wg ? 64 * nr : 16 * nr;
     units = mq_max_tiles(num_seqs, num_tokens, G, R) * num_kv_heads;
   } else {
     units = (long)num_tokens * num_kv_heads;
@@ -449,8 +463,20 @@ int pa_mq_attention(void* out, void* workspace, size_t workspace_bytes, const vo
   const size_t dws_bytes = workspace_bytes - mq_head_bytes(num_seqs, num_tokens, G);
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  const int nr = tiled ? mq_row_blocks(head_dim, G, max_query_len) : 1;
-  const int R = 16 * nr;
+  // More rows per (sequence, KV head) than one wavefront holds: the
+  // workgroup-shared kernel (four wavefronts of rows over shared K/V chunks).
+  // PA_MQ_WG=0/1 overrides.
+  int nr = tiled ? mq_row_blocks(head_dim, G, max_query_len) : 1;
+  const int nr_env = env_int("PA_MQ_NR", 0);
+  if (tiled && (nr_env == 1 || nr_env == 2 || nr_env == 4)) nr = nr_env;
+  const int wg_env = env_int("PA_MQ_WG", -1);
+  const bool wg = tiled && (wg_env >= 0 ? wg_env != 0
+                                        : (long)max_query_len * G > 16L * nr);
+  // the shared kernel keeps four row-wavefronts per SIMD resident: two row
+  // blocks at head_dim 64, one above (measured: a 2048-token prefill at
+  // head_dim 64 runs 1.6x faster with two blocks than with four)
+  if (wg && nr_env == 0) nr = head_dim == 64 ? (nr < 2 ? nr : 2) : 1;
+  const int R = wg ? 64 * nr : 16 * nr;
   pa::mq_plan_kernel<<<dim3(1), dim3(1024), 0, s>>>(
       query_start, context_lens, num_seqs, num_tokens, max_context_len, G, R,
       tiled ? tiles : nullptr, (int)mq_max_tiles(num_seqs, num_tokens, G, R), num_tiles, vctx,
@@ -506,16 +532,25 @@ int pa_mq_attention(void* out, void* workspace, size_t workspace_bytes, const vo
     p.num_tokens = num_tokens;
     const long blocks = max_tiles * num_kv_heads * np;
     if (blocks > 0x7fffffffL) return PA_EUNSUPPORTED;
-    const int tiles_per_chunk = block_size >= 32 && nr * head_dim <= 128 ? 2 : 1;
-    const size_t lds_wave = pa::mq_mfma_lds_bytes(head_dim, nr, tiles_per_chunk);
-    const int span = window > 0 && window < p.part ? window : p.part;
-    int nw = waves_for(span, 16 * tiles_per_chunk, (int)(blocks < (1L << 30) ? blocks : (1L << 30)));
-    while (nw > 1 && nw * lds_wave > 65536) nw /= 2;
     const dim3 grid((unsigned)blocks);
-    const bool ok =
-        dtype == PA_F16
-            ? pa::launch_mq_mfma_f16(head_dim, nr, tiles_per_chunk, nw, grid, s, p)
-            : pa::launch_mq_mfma_bf16(head_dim, nr, tiles_per_chunk, nw, grid, s, p);
+    bool ok;
+    if (wg) {
+      const int tiles_per_chunk = block_size >= 32 && head_dim <= 128 ? 2 : 1;
+      const int nbuf = env_int("PA_MQ_NBUF", 3);
+      ok = dtype == PA_F16
+               ? pa::launch_mq_wg_f16(head_dim, nr, tiles_per_chunk, nbuf, grid, s, p)
+               : pa::launch_mq_wg_bf16(head_dim, nr, tiles_per_chunk, nbuf, grid, s, p);
+    } else {
+      const int tiles_per_chunk = block_size >= 32 && nr * head_dim <= 128 ? 2 : 1;
+      const size_t lds_wave = pa::mq_mfma_lds_bytes(head_dim, nr, tiles_per_chunk);
+      const int span = window > 0 && window < p.part ? window : p.part;
+      int nw = waves_for(span, 16 * tiles_per_chunk,
+                         (int)(blocks < (1L << 30) ? blocks : (1L << 30)));
+      while (nw > 1 && nw * lds_wave > 65536) nw /= 2;
+      ok = dtype == PA_F16
+               ? pa::launch_mq_mfma_f16(head_dim, nr, tiles_per_chunk, nw, grid, s, p)
+               : pa::launch_mq_mfma_bf16(head_dim, nr, tiles_per_chunk, nw, grid, s, p);
+    }
     if (!ok) return PA_EUNSUPPORTED;
     rc = hipGetLastError() == hipSuccess ? PA_OK : PA_ELAUNCH;
   }

@@ -31,7 +31,7 @@ constexpr int kMaxWaves = 8;
 
 struct DecodeParams {
   void* out;               // [B, Hq, D]
-  const int32_t* order;      // [B] sequences, longest first (workspace)
+  const int32_t* order;      // [B] sequences, longest first (workspace); null: 0, 1, ...
   const int32_t* num_items;  // looping launches: number of work items
   const int2* items;         // looping launches: (sequence, partition) list
   float* tmp_out;          // [B, Hq, NP, D]
@@ -133,7 +133,7 @@ __device__ __forceinline__ bool grid_unit(const DecodeParams& p, Unit& u) {
   u.g = id % p.num_kv_heads;
   const int rest = id / p.num_kv_heads;
   u.part = rest / p.num_seqs;
-  u.b = ((cint32*)p.order)[rest % p.num_seqs];
+  u.b = p.order ? ((cint32*)p.order)[rest % p.num_seqs] : rest % p.num_seqs;
   return unit_range<DT, D, G>(p, u);
 }
 

@@ -30,6 +30,12 @@ bool launch_mq_mfma_bf16(int D, int nr, int tiles, int nw, dim3 grid, hipStream_
                          const MQParams& p);
 size_t mq_mfma_lds_bytes(int D, int nr, int tiles);
 
+// Workgroup-shared multi-query path (four wavefronts of 16 * nr rows each).
+bool launch_mq_wg_f16(int D, int nr, int tiles, int nbuf, dim3 grid, hipStream_t s,
+                      const MQParams& p);
+bool launch_mq_wg_bf16(int D, int nr, int tiles, int nbuf, dim3 grid, hipStream_t s,
+                       const MQParams& p);
+
 }  // namespace pa
 
 // Expands to the body of a launcher for storage type DT.
@@ -101,6 +107,27 @@ size_t mq_mfma_lds_bytes(int D, int nr, int tiles);
       PA_MQ_CASE(DT, 128, 1, 1) PA_MQ_CASE(DT, 128, 1, 2)                           \
       PA_MQ_CASE(DT, 128, 2, 1)                                                     \
       PA_MQ_CASE(DT, 256, 1, 1)                                                     \
+      default: return false;                                                        \
+    }                                                                               \
+  }
+
+#define PA_MQ_WG_CASE(DT, DV, NRV, TV, BV)                                          \
+  case ((DV * 8 + NRV) * 4 + TV) * 8 + BV:                                          \
+    mq_wg_kernel<DT, DV, NRV, TV, BV>                                               \
+        <<<grid, dim3(256), MQWGShape<DT, DV, NRV, TV, BV>::LDS_BYTES, s>>>(p);     \
+    return true;
+
+#define PA_DEFINE_MQ_WG_LAUNCHER(NAME, DT)                                          \
+  bool NAME(int D, int nr, int tiles, int nbuf, dim3 grid, hipStream_t s, const MQParams& p) { \
+    switch (((D * 8 + nr) * 4 + tiles) * 8 + nbuf) {                               \
+      PA_MQ_WG_CASE(DT, 64, 1, 1, 3) PA_MQ_WG_CASE(DT, 64, 1, 2, 3)                 \
+      PA_MQ_WG_CASE(DT, 64, 2, 1, 3) PA_MQ_WG_CASE(DT, 64, 2, 2, 3)                 \
+      PA_MQ_WG_CASE(DT, 64, 4, 1, 3) PA_MQ_WG_CASE(DT, 64, 4, 2, 3)                 \
+      PA_MQ_WG_CASE(DT, 64, 2, 2, 4) PA_MQ_WG_CASE(DT, 64, 4, 2, 4)                 \
+      PA_MQ_WG_CASE(DT, 128, 1, 1, 3) PA_MQ_WG_CASE(DT, 128, 1, 2, 3)               \
+      PA_MQ_WG_CASE(DT, 128, 2, 1, 3) PA_MQ_WG_CASE(DT, 128, 2, 2, 3)               \
+      PA_MQ_WG_CASE(DT, 256, 1, 1, 3) PA_MQ_WG_CASE(DT, 256, 2, 1, 3)               \
+      PA_MQ_WG_CASE(DT, 256, 1, 1, 4)                                               \
       default: return false;                                                        \
     }                                                                               \
   }

@@ -417,4 +417,317 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Workgroup-shared variant for many rows per (sequence, KV head): prompt
+// chunks and whole-prompt prefill.  Four wavefronts own consecutive 16 * NR
+// row blocks of one R = 64 * NR row tile and walk the same keys in lockstep:
+// each K and V chunk is copied HBM -> LDS once (the four wavefronts issue a
+// quarter of the direct-to-LDS loads each) and read by all of them, so the
+// pages are fetched once per R rows.  NBUF chunk buffers keep NBUF - 1
+// chunks in flight; one workgroup barrier per chunk publishes the next one.
+//   q.k  A = K fragments from LDS (16-byte reads; K rows stored with their
+//        16-byte segments XOR-swizzled so 16 rows hit distinct banks);
+//   P.V  A = V^T gathered from LDS as in the per-wavefront kernel.
+// A wavefront skips the arithmetic of chunks none of its rows attends to
+// (the causal upper triangle), but still loads and syncs.
+template <int DT, int D, int NR, int TILES, int NBUF_ = 3>
+struct MQWGShape {
+  static constexpr int NW = 4;                  // wavefronts per workgroup
+  static constexpr int RW = 16 * NR;            // rows per wavefront
+  static constexpr int R = NW * RW;             // rows per workgroup
+  static constexpr int NT = 16 * TILES;         // tokens per chunk
+  static constexpr int KS = D / 32;
+  static constexpr int MT = D / 16;
+  static constexpr int CBYTES = NT * D * 2;     // one K or V chunk
+  static constexpr int LOADS = CBYTES / 1024;   // 1 KB loads per K or V chunk
+  static constexpr int LPW = 2 * LOADS / NW;    // K + V loads per wavefront per chunk
+  static constexpr int NBUF = NBUF_;              // chunk buffers (NBUF - 1 in flight)
+  static constexpr int LDS_BYTES = NBUF * 2 * CBYTES;
+  static_assert(CBYTES % 1024 == 0 && (2 * LOADS) % NW == 0, "chunk shape");
+};
+
+// K rows in LDS: 16-byte segment s of row r is stored at s ^ k_swz(r)
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+  return D >= 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+template <int DT, int D, int NR, int TILES, int NBUF_>
+__global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
+  using S = MQWGShape<DT, D, NR, TILES, NBUF_>;
+  constexpr int NW = S::NW, RW = S::RW, R = S::R, NT = S::NT, KS = S::KS, MT = S::MT;
+  constexpr int CBYTES = S::CBYTES, LOADS = S::LOADS, LPW = S::LPW, NBUF = S::NBUF;
+  constexpr int EB = 2;
+  typedef const __attribute__((address_space(4))) int32_t cint32;
+  typedef const __attribute__((address_space(4))) uint64_t cu64;
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c16 = lane & 15;
+  const int j = lane >> 4;
+  extern __shared__ float smem[];
+  char* lds = reinterpret_cast<char*>(smem);
+
+  const int Hq = p.num_heads;
+  const int G = p.group;
+  const int g = blockIdx.x % p.num_kv_heads;
+  const int rest = blockIdx.x / p.num_kv_heads;
+  const int tile = rest % p.max_tiles;
+  const int part = rest / p.max_tiles;
+  if (tile >= *(cint32*)p.num_tiles) return;
+  const uint64_t tl = ((cu64*)p.tiles)[tile];
+  const int b = (int)(uint32_t)tl;
+  const int f0 = (int)(uint32_t)(tl >> 32);
+  const int q0 = min(max(((cint32*)p.query_start)[b], 0), p.num_tokens);
+  const int n = min(max(((cint32*)p.query_start)[b + 1] - q0, 0), p.num_tokens - q0);
+  const int f_end = min(f0 + R, n * G);
+  const int L = min(((cint32*)p.context_lens)[b], p.max_context_len);
+  const int W = p.window;
+  const int P = p.part;
+  auto key_lo = [&](int pos) { return W > 0 ? max(0, pos + 1 - W) : 0; };
+  const int i_first = f0 / G;
+  const int i_last = (f_end - 1) / G;
+  const int lo = max(key_lo(L - n + i_first), part * P);
+  const int hi = min(L - n + i_last + 1, part * P + P);
+  if (f0 >= f_end || lo >= hi) return;  // uniform over the workgroup
+
+  // this wavefront's rows: f0 + RW * w + 16 nb + c16
+  const int fw0 = f0 + RW * w;
+  int a_lo[NR], a_hi[NR];
+  uint4 qf[NR][KS];
+#pragma unroll
+  for (int nb = 0; nb < NR; ++nb) {
+    const int f = fw0 + 16 * nb + c16;
+    const bool act = f < f_end;
+    const int i = act ? f / G : i_first;
+    const int h = act ? f - i * G : 0;
+    const int pos = L - n + i;
+    a_lo[nb] = act ? max(lo, key_lo(pos)) : 0;
+    a_hi[nb] = act ? min(hi, pos + 1) : 0;
+    const char* qb = static_cast<const char*>(p.q) +
+                     (((size_t)(q0 + i) * Hq + (size_t)g * G + h) * D + 8 * j) * EB;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qf[nb][s] = act ? ld16(qb + (size_t)s * 32 * EB) : make_uint4(0, 0, 0, 0);
+  }
+  // keys this wavefront attends to at all (empty when it has no rows)
+  int wlo = hi, whi = lo;
+  if (fw0 < f_end) {
+    const int fl = min(fw0 + RW, f_end) - 1;
+    wlo = max(lo, key_lo(L - n + fw0 / G));
+    whi = min(hi, L - n + fl / G + 1);
+  }
+
+  const int32_t* bt = p.block_tables + (size_t)b * p.max_blocks_per_seq;
+  const int log2_bs = p.log2_bs;
+  const int last_pg = (hi - 1) >> log2_bs;
+  // 64 consecutive block-table entries, one per lane, read by lane index
+  int pg0 = -(1 << 30);
+  int tbl_v = 0;
+  const uint32_t row_bytes = (uint32_t)(p.num_kv_heads * D * EB);
+  const uint32_t page_bytes = row_bytes << log2_bs;
+  const uint32_t head_bytes = (uint32_t)(g * D * EB);
+  const char* kbase = static_cast<const char*>(p.k_cache);
+  const char* vbase = static_cast<const char*>(p.v_cache);
+  const char* dummy = static_cast<const char*>(p.q) +
+                      ((size_t)(q0 + i_first) * Hq + (size_t)g * G) * D * EB;
+
+  // this wavefront's share of a chunk's copies: loads q = LPW * w + k; the
+  // first LOADS are K, the rest V.  Lane l's 16 bytes land at byte
+  // 1024 (q % LOADS) + 16 l of the K or V chunk: row r, stored segment
+  // sg, global segment sg ^ swizzle(r).
+  int ld_row[LPW];
+  uint32_t ld_seg[LPW];
+#pragma unroll
+  for (int k = 0; k < LPW; ++k) {
+    const int q = LPW * w + k;
+    const int o = (q % LOADS) * 1024 + lane * 16;
+    const int r = o / (2 * D);
+    const int sg = (o % (2 * D)) >> 4;
+    ld_row[k] = r;
+    ld_seg[k] = head_bytes + (uint32_t)((sg ^ (q < LOADS ? k_swz<D>(r) : v_swz<D>(r))) * 16);
+  }
+  auto issue = [&](int c, int buf) {
+    rsrc_t kr, vr;
+    uint32_t soff = 0;
+    int rlo = 0, rhi = 0;
+    if (c * NT < hi) {
+      const int cs = c * NT;
+      const int cpg = max(cs, lo) >> log2_bs;
+      if (cpg < pg0 || cpg - pg0 >= 64) {
+        pg0 = cpg;
+        const int pg = cpg + lane;
+        tbl_v = pg <= last_pg ? bt[pg] : 0;
+      }
+      int phys = __builtin_amdgcn_readlane(tbl_v, cpg - pg0);
+      phys = ((unsigned)phys < (unsigned)p.num_blocks) ? phys : 0;
+      const uint64_t base = (uint64_t)phys * page_bytes;
+      kr = make_rsrc(kbase + base, page_bytes);
+      vr = make_rsrc(vbase + base, page_bytes);
+      soff = (uint32_t)(cs & ((1 << log2_bs) - 1)) * row_bytes;
+      rlo = lo - cs;
+      rhi = hi - 1 - cs;
+    } else {
+      kr = make_rsrc(dummy, (uint32_t)(G * D * EB));
+      vr = kr;
+    }
+    char* kb = lds + buf * 2 * CBYTES;
+#pragma unroll
+    for (int k = 0; k < LPW; ++k) {
+      const int q = LPW * w + k;
+      const int r = min(max(ld_row[k], rlo), rhi);
+      const bool is_k = q < LOADS;
+      ld16_buf_to_lds(is_k ? kr : vr, kb + (is_k ? 0 : CBYTES) + (q % LOADS) * 1024,
+                      (uint32_t)r * row_bytes + ld_seg[k], soff);
+    }
+  };
+
+  float m_run[NR], l_run[NR];
+  f32x4_t acc[NR][MT];
+#pragma unroll
+  for (int nb = 0; nb < NR; ++nb) {
+    m_run[nb] = kNegInf;
+    l_run[nb] = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  const int c0 = lo / NT;
+  const int c1 = (hi - 1) / NT;
+#pragma unroll
+  for (int k = 0; k < NBUF - 1; ++k) issue(c0 + k, k);
+  int buf = 0;
+#pragma clang loop unroll(disable)
+  for (int c = c0; c <= c1; ++c) {
+    // this wavefront's copies of chunk c are done; the barrier makes every
+    // wavefront's copies visible, and every wavefront is past chunk c - 1,
+    // so its buffer can take chunk c + NBUF - 1
+    __builtin_amdgcn_s_waitcnt(vmcnt_only((NBUF - 2) * LPW));
+    __syncthreads();
+    issue(c + NBUF - 1, buf == 0 ? NBUF - 1 : buf - 1);
+    const char* kb = lds + buf * 2 * CBYTES;
+    const char* vb = kb + CBYTES;
+    buf = buf == NBUF - 1 ? 0 : buf + 1;
+    const int cs = c * NT;
+    if (wlo >= whi || cs + NT <= wlo || cs >= whi) continue;  // no row of this wavefront looks here
+
+    f32x4_t sc[NR][TILES];
+#pragma unroll
+    for (int nb = 0; nb < NR; ++nb)
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) sc[nb][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int r = 16 * t + c16;
+        const uint4 kf = *reinterpret_cast<const uint4*>(
+            kb + r * 2 * D + (((4 * s + j) ^ k_swz<D>(r)) << 4));
+#pragma unroll
+        for (int nb = 0; nb < NR; ++nb) sc[nb][t] = mfma_k32<DT>(kf, qf[nb][s], sc[nb][t]);
+      }
+
+    uint32_t pk[NR][2 * TILES];
+#pragma unroll
+    for (int nb = 0; nb < NR; ++nb) {
+      float pr[TILES][4];
+      if (p.cap_mul > 0.0f) {
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pr[t][i] = p.cap_mul * tanh_def(sc[nb][t][i] * p.qk_mul);
+      } else {
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pr[t][i] = sc[nb][t][i] * p.qk_mul;
+      }
+      float cmax = kNegInf;
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pos = cs + 16 * t + 4 * j + i;
+          pr[t][i] = (pos >= a_lo[nb] && pos < a_hi[nb]) ? pr[t][i] : kNegInf;
+          cmax = fmaxf(cmax, pr[t][i]);
+        }
+      cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
+      cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
+      const float m_new = fmaxf(m_run[nb], cmax);
+      const float m_use = m_new == kNegInf ? 0.0f : m_new;
+      const float alpha = fast_exp2(m_run[nb] - m_use);
+      float psum = 0.0f;
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pr[t][i] = fast_exp2(pr[t][i] - m_use);
+          psum += pr[t][i];
+        }
+      l_run[nb] = l_run[nb] * alpha + psum;
+      m_run[nb] = m_new;
+      if (any_rescale(alpha)) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[nb][mt] *= alpha;
+      }
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        pk[nb][2 * t] = pack2<DT>(pr[t][0], pr[t][1]);
+        pk[nb][2 * t + 1] = pack2<DT>(pr[t][2], pr[t][3]);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      uint32_t vv[2 * TILES];
+      vt_frag<D, TILES>(vb, mt, c16, j, vv);
+#pragma unroll
+      for (int nb = 0; nb < NR; ++nb) {
+        if constexpr (TILES == 2)
+          acc[nb][mt] = mfma_k32<DT>(make_uint4(vv[0], vv[1], vv[2], vv[3]),
+                                     make_uint4(pk[nb][0], pk[nb][1], pk[nb][2], pk[nb][3]),
+                                     acc[nb][mt]);
+        else
+          acc[nb][mt] = mfma_k16<DT>(make_uint2(vv[0], vv[1]), make_uint2(pk[nb][0], pk[nb][1]),
+                                     acc[nb][mt]);
+      }
+    }
+  }
+  // the copies issued past the last chunk must land before the workgroup
+  // (and its LDS) goes away
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // ---- epilogue: each wavefront writes its own rows ----
+#pragma unroll
+  for (int nb = 0; nb < NR; ++nb) {
+    float l = l_run[nb];
+    l += shfl_xor_f(l, 16);
+    l += shfl_xor_f(l, 32);
+    const int f = fw0 + 16 * nb + c16;
+    if (f >= f_end || l == 0.0f) continue;  // past the end, or no key here
+    const float inv = 1.0f / l;
+    const int i = f / G;
+    const int h = f - i * G;
+    const int pos = L - n + i;
+    const size_t row = (size_t)(q0 + i) * Hq + (size_t)g * G + h;
+    if (key_lo(pos) / P == pos / P) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const size_t e = row * D + 16 * mt + 4 * j;
+        const uint2 v = make_uint2(pack2<DT>(acc[nb][mt][0] * inv, acc[nb][mt][1] * inv),
+                                   pack2<DT>(acc[nb][mt][2] * inv, acc[nb][mt][3] * inv));
+        *reinterpret_cast<uint2*>(static_cast<char*>(p.out) + e * EB) = v;
+      }
+    } else {
+      const size_t pi = row * p.num_parts + part;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        *reinterpret_cast<f32x4_t*>(p.tmp_out + pi * D + 16 * mt + 4 * j) = acc[nb][mt] * inv;
+      if (j == 0) {
+        p.max_logits[pi] = m_run[nb];
+        p.exp_sums[pi] = l;
+      }
+    }
+  }
+}
+
 }  // namespace pa

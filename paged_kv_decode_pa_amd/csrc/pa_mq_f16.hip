@@ -3,6 +3,7 @@
 
 namespace pa {
 PA_DEFINE_MQ_LAUNCHER(launch_mq_mfma_f16, DT_F16)
+PA_DEFINE_MQ_WG_LAUNCHER(launch_mq_wg_f16, DT_F16)
 size_t mq_mfma_lds_bytes(int D, int nr, int tiles) {
   // identical for f16 and bf16 (MQShape::LDS_FLOATS)
   const int vf = 2 * (16 * tiles * D * 2) / 4;

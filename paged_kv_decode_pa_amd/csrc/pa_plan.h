@@ -130,7 +130,10 @@ __global__ __launch_bounds__(1024) void mq_plan_kernel(const int32_t* __restrict
       }
       int total;
       const int off = base + block_exclusive_scan(nt, s_tmp, &total);
-      for (int i = 0; i < nt && off + i < tile_cap; ++i) tiles[off + i] = make_int2(b, i * R);
+      // a sequence's last rows see the most keys: list them first, so the
+      // longest tiles start first
+      for (int i = 0; i < nt && off + i < tile_cap; ++i)
+        tiles[off + i] = make_int2(b, (nt - 1 - i) * R);
       base += total;
     }
     if (t == 0) *num_tiles = min(base, tile_cap);

@@ -36,12 +36,16 @@ class DeviceMQ:
             self.value = upload(c.value, c.dtype)
             self.slots = torch.from_numpy(c.slot_mapping).cuda()
 
-    def run(self, partition_size=None, tiled=None, out=None, max_query_len=None):
+    def run(self, partition_size=None, tiled=None, out=None, max_query_len=None, shared=None):
+        """tiled: matrix-core path (True) or per token (False); shared: force
+        the workgroup-shared (True) or per-wavefront (False) tiled kernel."""
         import torch
         import paged_kv_decode_pa_amd as pa
         c = self.c
         if tiled is not None:
             os.environ["PA_MQ_TILED"] = "1" if tiled else "0"
+        if shared is not None:
+            os.environ["PA_MQ_WG"] = "1" if shared else "0"
         try:
             if self.slots is not None:
                 pa.reshape_and_cache(self.key, self.value, self.k_cache, self.v_cache, self.slots)
@@ -53,6 +57,7 @@ class DeviceMQ:
             torch.cuda.synchronize()
         finally:
             os.environ.pop("PA_MQ_TILED", None)
+            os.environ.pop("PA_MQ_WG", None)
         return out
 
 
@@ -86,19 +91,24 @@ def _id(s):
     return f"{s[0]}-g{s[1]}-d{s[2]}-bs{s[3]}-c{int(s[4])}-w{s[5]}-p{s[6]}"
 
 
+PATHS = {"shared": (True, True), "wave": (True, False), "auto": (True, None),
+         "pertoken": (False, None)}
+
+
 @pytest.mark.parametrize("shape", SHAPES, ids=[_id(s) for s in SHAPES])
-@pytest.mark.parametrize("tiled", [True, False], ids=["tiled", "pertoken"])
-def test_mq_shapes(shape, tiled):
+@pytest.mark.parametrize("path", list(PATHS))
+def test_mq_shapes(shape, path):
     from gpu_util import say
     dtype, G, D, bs, cap, W, P, L, n = shape
+    tiled, shared = PATHS[path]
     if not tiled and G not in (1, 2, 4, 8, 16):
         pytest.skip("the per-token path takes the decode group sizes")
-    say(f"mq {_id(shape)} tiled={tiled}")
+    say(f"mq {_id(shape)} path={path}")
     Hkv = 2
     c = make_mq_case(Hq=G * Hkv, Hkv=Hkv, D=D, bs=bs, dtype=dtype, context_lens=L, query_lens=n,
                      softcap=cap, window=W, partition_size=P, seed=D + G + bs + W,
                      new_rows=True)
-    got = DeviceMQ(c).run(tiled=tiled)
+    got = DeviceMQ(c).run(tiled=tiled, shared=shared)
     check(got, oracle.multi_query_case(c), dtype)
 
 
@@ -139,8 +149,8 @@ def test_mq_empty_sequences_and_no_tokens():
     say("mq empty sequences")
     c = make_mq_case(Hq=4, Hkv=2, D=64, bs=16, dtype="bf16", context_lens=[20, 0, 35, 9],
                      query_lens=[4, 0, 0, 9], partition_size=16, seed=2, new_rows=True)
-    for tiled in (True, False):
-        check(DeviceMQ(c).run(tiled=tiled), oracle.multi_query_case(c), "bf16")
+    for tiled, shared in ((True, True), (True, False), (False, None)):
+        check(DeviceMQ(c).run(tiled=tiled, shared=shared), oracle.multi_query_case(c), "bf16")
     z = make_mq_case(Hq=4, Hkv=2, D=64, bs=16, dtype="bf16", context_lens=[20, 7],
                      query_lens=[0, 0], seed=3)
     out = DeviceMQ(z).run()
