@@ -31,7 +31,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_decode_gemma2_b512_traffic.md")
+# committed rocprofv3 counter summaries (HBM bytes per launch) by workload
+TRAFFIC_FILES = {
+    "4": os.path.join(ROOT, "profiles", "pa_decode_gemma2_b512_traffic.md"),
+    "spec5": os.path.join(ROOT, "profiles", "pa_mq_gemma2_spec5_b512_traffic.md"),
+}
 
 
 def kernel_source_digest() -> str:
@@ -44,12 +48,13 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(digest: str):
-    """HBM bytes per decode launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel sources."""
+def measured_traffic(digest: str, workload: str):
+    """HBM bytes per launch of the workload's attention call from the
+    committed rocprofv3 counter summary, if it was taken on the current
+    kernel sources."""
     try:
-        text = open(TRAFFIC_FILE).read()
-    except OSError:
+        text = open(TRAFFIC_FILES[workload]).read()
+    except (KeyError, OSError):
         return None
     vals = {}
     for line in text.splitlines():
@@ -109,6 +114,19 @@ def cpu_baseline(case, budget_s: float):
 
 
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}
+
+
+def calibration_copy(mib: int, dev):
+    """Three plain device copies of `mib` MiB: the yardstick that scales the
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] calibration copy: 3 x {mib} MiB read + write", file=sys.stderr, flush=True)
 
 
 def cpu_baseline_mq(case, budget_s: float):
@@ -209,6 +227,8 @@ def bench_mq(args):
     attn_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
     print(f"[bench] timed {args.steps} steps: {ms_step*1e3:.1f} us/step wall, "
           f"pa_mq_attention {attn_ms*1e3:.1f} us (HIP events)", file=sys.stderr, flush=True)
+    if args.calib_copy_mib:
+        calibration_copy(args.calib_copy_mib, dev)
 
     max_err = None
     if not args.no_check:
@@ -246,9 +266,11 @@ def bench_mq(args):
         achieved = ab["attn"] / (attn_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof.update({"traffic": None, "kernel": "pa_mq_attention (plan + attention + reduce)",
+    digest = kernel_source_digest()
+    roof.update({"traffic": measured_traffic(digest, args.workload),
+                 "kernel": "pa_mq_attention (plan + attention + reduce)",
                  "algorithmic_bytes_per_launch": ab["attn"], "flops_per_launch": flops,
-                 "flop_per_byte": round(intensity, 2), "kernel_sources": kernel_source_digest()})
+                 "flop_per_byte": round(intensity, 2), "kernel_sources": digest})
     cpu = None
     if args.cpu_budget > 0:
         print(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s)", file=sys.stderr,
@@ -398,14 +420,7 @@ def main():
         print(f"[bench] graph replay: {g_ms*1e3:.1f} us/step", file=sys.stderr, flush=True)
 
     if args.calib_copy_mib:
-        n = args.calib_copy_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"[bench] calibration copy: 3 x {args.calib_copy_mib} MiB read + write",
-              file=sys.stderr, flush=True)
+        calibration_copy(args.calib_copy_mib, dev)
 
     max_err = None
     if not args.no_check:
@@ -426,7 +441,7 @@ def main():
     value = ab["total"] / step_s / 1e9
     achieved = ab["decode"] / (decode_ms / 1e3) / 1e9
     digest = kernel_source_digest()
-    traffic = measured_traffic(digest)
+    traffic = measured_traffic(digest, str(args.workload))
 
     cpu = None
     if args.cpu_budget > 0:

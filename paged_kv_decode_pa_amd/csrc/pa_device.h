@@ -19,6 +19,7 @@ constexpr float kNegInf = -__builtin_huge_valf();
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // 16-byte fragments: one lane's share of a K/V/q row

@@ -501,16 +501,19 @@ __global__ __launch_bounds__(64 * kMaxWaves, PA_DECODE_MIN_WAVES) void decode_ke
 }
 
 // One workgroup of four wavefronts per (sequence, query head): merge the
-// partials of sequences that span more than one non-empty partition.  The
-// wavefronts split the partitions (four loads in flight each), lanes split
-// head_dim, and the four partial sums meet in LDS.
+// partials of sequences that span more than one non-empty partition.  A
+// partial row (D floats) is read as float4 by D/4 lanes, so a wavefront
+// takes 64/(D/4) partitions per step and the four wavefronts interleave;
+// the per-lane sums meet through xor shuffles and LDS.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
-  constexpr int EPL = D / 64;
+  constexpr int LPP = D / 4;     // lanes per partition row
+  constexpr int PPW = 64 / LPP;  // partition rows per wavefront step
+  constexpr int NWV = 4;
   typedef const __attribute__((address_space(4))) float cfloat;
-  __shared__ float s_red[4];
-  __shared__ float s_o[4][D];
-  __shared__ float s_den[4];
+  __shared__ float s_red[NWV];
+  __shared__ float s_o[NWV][D];
+  __shared__ float s_den[NWV];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -536,20 +539,27 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
   __syncthreads();
   M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
 
-  float o[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) o[e] = 0.0f;
+  const int sub = lane / LPP;  // which of the step's partitions
+  const int dl = lane % LPP;   // float4 of the row
+  f32x4_t o = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   float den = 0.0f;
-  const float* src = p.tmp_out + base * D + lane * EPL;
+  const float* src = p.tmp_out + base * D + 4 * dl;
 #pragma unroll 4
-  for (int q = p0 + w; q <= p1; q += 4) {
+  for (int q = p0 + w * PPW + sub; q <= p1; q += NWV * PPW) {
     const float wq = es[q] * fast_exp2(ml[q] - M);
-    den += wq;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] = fmaf(wq, src[(size_t)q * D + e], o[e]);
+    den += dl == 0 ? wq : 0.0f;
+    o += wq * *reinterpret_cast<const f32x4_t*>(src + (size_t)q * D);
   }
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) s_o[w][lane * EPL + e] = o[e];
+  for (int m = LPP; m < 64; m <<= 1) {
+    o[0] += shfl_xor_f(o[0], m);
+    o[1] += shfl_xor_f(o[1], m);
+    o[2] += shfl_xor_f(o[2], m);
+    o[3] += shfl_xor_f(o[3], m);
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) den += shfl_xor_f(den, m);
+  if (sub == 0) *reinterpret_cast<f32x4_t*>(&s_o[w][4 * dl]) = o;
   if (lane == 0) s_den[w] = den;
   __syncthreads();
   const float inv = 1.0f / (s_den[0] + s_den[1] + s_den[2] + s_den[3]);

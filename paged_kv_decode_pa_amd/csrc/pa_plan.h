@@ -42,14 +42,33 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_tmp, int* tota
   return r;
 }
 
+// Expands nk lists into one array of `total` entries, all threads writing:
+// list k starts at s_off[k] (exclusive offsets, non-decreasing) and ends
+// where the next list starts, so entry idx belongs to the last k with
+// s_off[k] <= idx.  emit(k, i, idx) writes entry i of list k at idx.
+template <typename Emit>
+__device__ __forceinline__ void expand_lists(const int* s_off, int nk, int total, Emit&& emit) {
+  for (int idx = threadIdx.x; idx < total; idx += blockDim.x) {
+    int lo = 0, hi = nk - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid] <= idx) lo = mid;
+      else hi = mid - 1;
+    }
+    emit(lo, idx - s_off[lo], idx);
+  }
+}
+
 // part: partition size in tokens (max_context_len when keys are not split)
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ context_lens,
                                                     int num_seqs, int max_context_len, int window,
                                                     int part, Plan plan) {
   constexpr int NBK = 256;
   __shared__ int hist[NBK];
-  __shared__ int offs[NBK];
   __shared__ int s_tmp[17];
+  __shared__ int s_off[1024];
+  __shared__ int s_seq[1024];
+  __shared__ int s_first[1024];
   const int t = threadIdx.x;
   if (t < NBK) hist[t] = 0;
   __syncthreads();
@@ -58,22 +77,20 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   // counting sort over 256 length buckets, descending: the longest
   // sequences land in bucket 0 (order within a bucket is arbitrary, which
   // no result depends on)
-  auto bucket = [&](int b) {
-    int n = length(b);
-    if (window > 0) n = min(n, window);
+  auto bucket = [&](int L) {
+    const int n = window > 0 ? min(L, window) : L;
     return NBK - 1 - (int)(((long long)n * (NBK - 1)) / span);
   };
-  for (int b = t; b < num_seqs; b += blockDim.x) atomicAdd(&hist[bucket(b)], 1);
+  for (int b = t; b < num_seqs; b += blockDim.x) atomicAdd(&hist[bucket(length(b))], 1);
   __syncthreads();
-  if (t == 0) {
-    int run = 0;
-    for (int k = 0; k < NBK; ++k) {
-      offs[k] = run;
-      run += hist[k];
-    }
+  {
+    int total;
+    const int off = block_exclusive_scan(t < NBK ? hist[t] : 0, s_tmp, &total);
+    if (t < NBK) hist[t] = off;
   }
   __syncthreads();
-  for (int b = t; b < num_seqs; b += blockDim.x) plan.order[atomicAdd(&offs[bucket(b)], 1)] = b;
+  for (int b = t; b < num_seqs; b += blockDim.x)
+    plan.order[atomicAdd(&hist[bucket(length(b))], 1)] = b;
   if (plan.items == nullptr) return;
   __syncthreads();
 
@@ -95,9 +112,16 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
       }
     }
     int total;
-    const int off = base + block_exclusive_scan(n, s_tmp, &total);
-    for (int i = 0; i < n; ++i) plan.items[off + i] = make_int2(b, first + i);
+    s_off[t] = block_exclusive_scan(n, s_tmp, &total);
+    s_seq[t] = b;
+    s_first[t] = first;
+    __syncthreads();
+    int2* items = plan.items + base;
+    expand_lists(s_off, blockDim.x, total, [&](int kk, int i, int idx) {
+      items[idx] = make_int2(s_seq[kk], s_first[kk] + i);
+    });
     base += total;
+    __syncthreads();
   }
   if (t == 0) *plan.num_items = base;
 }
@@ -106,8 +130,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
 //   vctx[tok] = context of query token tok (its position + 1, clamped to
 //   [0, max_context_len]); vrow[tok] = its sequence (per-token path);
 //   tiles = (sequence, first row) for every R rows of each sequence's
-//   n * G rows (tiled path), at most tile_cap of them.  Null outputs are
-//   skipped.
+//   n * G rows (tiled path), at most tile_cap of them, a sequence's last
+//   rows (the most keys) first.  Null outputs are skipped.
 __global__ __launch_bounds__(1024) void mq_plan_kernel(const int32_t* __restrict__ query_start,
                                                        const int32_t* __restrict__ context_lens,
                                                        int num_seqs, int num_tokens,
@@ -115,8 +139,17 @@ __global__ __launch_bounds__(1024) void mq_plan_kernel(const int32_t* __restrict
                                                        int2* tiles, int tile_cap,
                                                        int32_t* num_tiles, int32_t* vctx,
                                                        int32_t* vrow) {
+  constexpr int kQS = 4096;  // sequence starts searched in LDS up to this many sequences
   __shared__ int s_tmp[17];
+  __shared__ int s_off[1024];
+  __shared__ int s_nt[1024];
+  __shared__ int s_qs[kQS + 1];
   const int t = threadIdx.x;
+  const bool in_lds = num_seqs + 1 <= kQS + 1;
+  if (in_lds)
+    for (int b = t; b <= num_seqs; b += blockDim.x) s_qs[b] = query_start[b];
+  __syncthreads();
+  auto qstart = [&](int b) { return in_lds ? s_qs[b] : query_start[b]; };
   if (tiles != nullptr) {
     int base = 0;
     for (int k0 = 0; k0 < num_seqs; k0 += blockDim.x) {
@@ -124,17 +157,20 @@ __global__ __launch_bounds__(1024) void mq_plan_kernel(const int32_t* __restrict
       int nt = 0;
       if (b < num_seqs) {
         // rows of the sequence's tokens that lie in [0, num_tokens)
-        const int q0 = min(max(query_start[b], 0), num_tokens);
-        const int n = min(max(query_start[b + 1] - q0, 0), num_tokens - q0);
+        const int q0 = min(max(qstart(b), 0), num_tokens);
+        const int n = min(max(qstart(b + 1) - q0, 0), num_tokens - q0);
         nt = (n * G + R - 1) / R;
       }
       int total;
-      const int off = base + block_exclusive_scan(nt, s_tmp, &total);
-      // a sequence's last rows see the most keys: list them first, so the
-      // longest tiles start first
-      for (int i = 0; i < nt && off + i < tile_cap; ++i)
-        tiles[off + i] = make_int2(b, (nt - 1 - i) * R);
+      s_off[t] = block_exclusive_scan(nt, s_tmp, &total);
+      s_nt[t] = nt;
+      __syncthreads();
+      const int room = max(tile_cap - base, 0);
+      expand_lists(s_off, blockDim.x, min(total, room), [&](int kk, int i, int idx) {
+        tiles[base + idx] = make_int2(k0 + kk, (s_nt[kk] - 1 - i) * R);
+      });
       base += total;
+      __syncthreads();
     }
     if (t == 0) *num_tiles = min(base, tile_cap);
   }
@@ -143,11 +179,12 @@ __global__ __launch_bounds__(1024) void mq_plan_kernel(const int32_t* __restrict
     int lo = 0, hi = num_seqs - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (query_start[mid] <= tok) lo = mid;
+      if (qstart(mid) <= tok) lo = mid;
       else hi = mid - 1;
     }
-    const int n = query_start[lo + 1] - query_start[lo];
-    const int pos = context_lens[lo] - n + (tok - query_start[lo]);
+    const int q0 = qstart(lo);
+    const int n = qstart(lo + 1) - q0;
+    const int pos = context_lens[lo] - n + (tok - q0);
     vctx[tok] = min(max(pos + 1, 0), max_context_len);
     if (vrow != nullptr) vrow[tok] = lo;
   }
