@@ -16,6 +16,12 @@ namespace {
 // MI355X: 256 compute units.  Used only to size work, never for correctness.
 constexpr int kNumCUs = 256;
 
+// LDS bytes a multi-wavefront workgroup may take (of 160 KB per CU), so that
+// at least two workgroups share a CU.
+#ifndef PA_WG_LDS_CAP
+#define PA_WG_LDS_CAP 65536
+#endif
+
 bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
 
 int ilog2(int v) {
@@ -240,9 +246,16 @@ static int decode_impl(void* out, void* workspace, size_t workspace_bytes, const
                                : decode_lds_bytes(dtype, head_dim, G);
   const int span = window > 0 && window < p.part ? window : p.part;
   const long units = (long)num_seqs * num_kv_heads * np;
-  int nw = waves_for(span, nt, (int)(units < (1L << 30) ? units : (1L << 30)));
-  while (nw > 1 && nw * lds_wave > 65536) nw /= 2;
-  const long blocks = (long)num_seqs * num_kv_heads * np;
+  // Matrix-core path: one wavefront per KV head in a workgroup, so the
+  // heads' adjacent rows of a token are fetched together (PA_DECODE_HEADS=0
+  // switches it off)
+  const bool heads = mfma && num_kv_heads <= pa::kMaxWaves &&
+                     (size_t)num_kv_heads * lds_wave <= PA_WG_LDS_CAP &&
+                     env_int("PA_DECODE_HEADS", 1) != 0;
+  int nw = heads ? num_kv_heads
+                 : waves_for(span, nt, (int)(units < (1L << 30) ? units : (1L << 30)));
+  while (!heads && nw > 1 && nw * lds_wave > PA_WG_LDS_CAP) nw /= 2;
+  const long blocks = (long)num_seqs * (heads ? 1 : num_kv_heads) * np;
   if (blocks > 0x7fffffffL) return PA_EUNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // One workgroup per (sequence, KV head, partition), unless that grid is
@@ -272,8 +285,9 @@ static int decode_impl(void* out, void* workspace, size_t workspace_bytes, const
   const bool paged = block_size >= nt;
   bool ok = false;
   if (mfma) {
-    ok = dtype == PA_F16 ? pa::launch_decode_mfma_f16(head_dim, G, tiles, loop, nw, grid, s, p)
-                         : pa::launch_decode_mfma_bf16(head_dim, G, tiles, loop, nw, grid, s, p);
+    ok = dtype == PA_F16
+             ? pa::launch_decode_mfma_f16(head_dim, G, tiles, loop, heads, nw, grid, s, p)
+             : pa::launch_decode_mfma_bf16(head_dim, G, tiles, loop, heads, nw, grid, s, p);
   } else {
     switch (dtype) {
       case PA_F32: ok = pa::launch_decode_f32(head_dim, G, paged, loop, grid, block, s, p); break;
@@ -546,7 +560,7 @@ int pa_mq_attention(void* out, void* workspace, size_t workspace_bytes, const vo
       const int span = window > 0 && window < p.part ? window : p.part;
       int nw = waves_for(span, 16 * tiles_per_chunk,
                          (int)(blocks < (1L << 30) ? blocks : (1L << 30)));
-      while (nw > 1 && nw * lds_wave > 65536) nw /= 2;
+      while (nw > 1 && nw * lds_wave > PA_WG_LDS_CAP) nw /= 2;
       ok = dtype == PA_F16
                ? pa::launch_mq_mfma_f16(head_dim, nr, tiles_per_chunk, nw, grid, s, p)
                : pa::launch_mq_mfma_bf16(head_dim, nr, tiles_per_chunk, nw, grid, s, p);

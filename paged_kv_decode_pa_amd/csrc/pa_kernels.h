@@ -105,13 +105,16 @@ struct Unit {
 };
 
 // Fills the unit's key range.  Returns false when it has no keys to attend
-// to; partition 0 of an empty sequence writes its zero output.
-template <int DT, int D, int G>
+// to; partition 0 of an empty sequence writes its zero output (by the whole
+// workgroup, or with HEADS by the head's own wavefront).
+template <int DT, int D, int G, bool HEADS = false>
 __device__ __forceinline__ bool unit_range(const DecodeParams& p, Unit& u) {
   const int L = min(p.context_lens[u.b], p.max_context_len);
   if (L <= 0) {
+    const int first = HEADS ? (int)(threadIdx.x & 63) : (int)threadIdx.x;
+    const int stride = HEADS ? 64 : (int)blockDim.x;
     if (u.part == 0)
-      for (int i = threadIdx.x; i < G * D; i += blockDim.x)
+      for (int i = first; i < G * D; i += stride)
         store_elem<DT>(p.out, ((size_t)u.b * p.num_heads + (size_t)u.g * G) * D + i, 0.0f);
     return false;
   }
@@ -125,46 +128,48 @@ __device__ __forceinline__ bool unit_range(const DecodeParams& p, Unit& u) {
 
 // One unit per workgroup: KV head fastest, then sequences in the plan's
 // longest-first order, then partitions (so a sequence's partitions are
-// spread over the whole dispatch).
-template <int DT, int D, int G>
+// spread over the whole dispatch).  HEADS: the workgroup holds every KV head
+// of its (sequence, partition), wavefront w taking head w.
+template <int DT, int D, int G, bool HEADS = false>
 __device__ __forceinline__ bool grid_unit(const DecodeParams& p, Unit& u) {
   typedef const __attribute__((address_space(4))) int32_t cint32;
   const int id = blockIdx.x;
-  u.g = id % p.num_kv_heads;
-  const int rest = id / p.num_kv_heads;
+  u.g = HEADS ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : id % p.num_kv_heads;
+  const int rest = HEADS ? id : id / p.num_kv_heads;
   u.part = rest / p.num_seqs;
   u.b = p.order ? ((cint32*)p.order)[rest % p.num_seqs] : rest % p.num_seqs;
-  return unit_range<DT, D, G>(p, u);
+  return unit_range<DT, D, G, HEADS>(p, u);
 }
 
-// Unit `it` of a looping launch: KV head fastest over the plan's item list.
-template <int DT, int D, int G>
+// Unit `it` of a looping launch: KV head fastest over the plan's item list
+// (HEADS: item `it` for every head, head = wavefront).
+template <int DT, int D, int G, bool HEADS = false>
 __device__ __forceinline__ bool item_unit(const DecodeParams& p, int it, Unit& u) {
   typedef const __attribute__((address_space(4))) uint64_t cu64;
-  u.g = it % p.num_kv_heads;
+  u.g = HEADS ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : it % p.num_kv_heads;
   // an item is (sequence, partition) as two int32, little-endian
-  const uint64_t item = ((cu64*)p.items)[it / p.num_kv_heads];
+  const uint64_t item = ((cu64*)p.items)[HEADS ? it : it / p.num_kv_heads];
   u.b = (int)(uint32_t)item;
   u.part = (int)(uint32_t)(item >> 32);
-  return unit_range<DT, D, G>(p, u);
+  return unit_range<DT, D, G, HEADS>(p, u);
 }
 
 // Runs body(unit) for this workgroup's units: its own one, or (LOOP) every
 // gridDim-th unit of the plan's list, so that a launch whose grid would be
 // mostly empty partitions stays small.
-template <int DT, int D, int G, bool LOOP, typename Body>
+template <int DT, int D, int G, bool LOOP, bool HEADS = false, typename Body>
 __device__ __forceinline__ void for_units(const DecodeParams& p, Body&& body) {
   if constexpr (LOOP) {
     typedef const __attribute__((address_space(4))) int32_t cint32;
-    const int n = *(cint32*)p.num_items * p.num_kv_heads;
+    const int n = *(cint32*)p.num_items * (HEADS ? 1 : p.num_kv_heads);
     for (int it = blockIdx.x; it < n; it += gridDim.x) {
       Unit u;
-      if (item_unit<DT, D, G>(p, it, u)) body(u);
+      if (item_unit<DT, D, G, HEADS>(p, it, u)) body(u);
       __syncthreads();  // LDS is reused by the next unit
     }
   } else {
     Unit u;
-    if (grid_unit<DT, D, G>(p, u)) body(u);
+    if (grid_unit<DT, D, G, HEADS>(p, u)) body(u);
   }
 }
 

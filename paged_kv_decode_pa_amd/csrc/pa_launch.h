@@ -16,10 +16,11 @@ bool launch_decode_bf16(int D, int G, bool paged, bool loop, dim3 grid, dim3 blo
 
 // Matrix-core path (f16/bf16, G in {8, 16}, block_size >= 16); returns
 // false when not built for the shape.
-bool launch_decode_mfma_f16(int D, int G, int tiles, bool loop, int nw, dim3 grid, hipStream_t s,
-                            const DecodeParams& p);
-bool launch_decode_mfma_bf16(int D, int G, int tiles, bool loop, int nw, dim3 grid, hipStream_t s,
-                             const DecodeParams& p);
+// heads: one wavefront per KV head (nw = num_kv_heads).
+bool launch_decode_mfma_f16(int D, int G, int tiles, bool loop, bool heads, int nw, dim3 grid,
+                            hipStream_t s, const DecodeParams& p);
+bool launch_decode_mfma_bf16(int D, int G, int tiles, bool loop, bool heads, int nw, dim3 grid,
+                             hipStream_t s, const DecodeParams& p);
 size_t decode_mfma_lds_bytes(int D, int G, int tiles);
 
 // Tiled multi-query path (f16/bf16, block_size >= 16 * tiles); nr 16-row
@@ -69,14 +70,16 @@ bool launch_mq_wg_bf16(int D, int nr, int tiles, int nbuf, dim3 grid, hipStream_
   case (DV * 32 + GV) * 4 + TV: {                                                   \
     const size_t lds = (size_t)nw * sizeof(float) *                                 \
                        MfmaShape<DT, DV, GV, TV>::LDS_FLOATS;                       \
-    if (loop) decode_mfma_kernel<DT, DV, GV, TV, true><<<grid, dim3(64 * nw), lds, s>>>(p);  \
+    if (heads && loop) decode_mfma_kernel<DT, DV, GV, TV, true, true><<<grid, dim3(64 * nw), lds, s>>>(p); \
+    else if (heads) decode_mfma_kernel<DT, DV, GV, TV, false, true><<<grid, dim3(64 * nw), lds, s>>>(p); \
+    else if (loop) decode_mfma_kernel<DT, DV, GV, TV, true><<<grid, dim3(64 * nw), lds, s>>>(p); \
     else decode_mfma_kernel<DT, DV, GV, TV, false><<<grid, dim3(64 * nw), lds, s>>>(p);     \
     return true;                                                                    \
   }
 
 #define PA_DEFINE_MFMA_LAUNCHER(NAME, DT)                                           \
-  bool NAME(int D, int G, int tiles, bool loop, int nw, dim3 grid, hipStream_t s,   \
-            const DecodeParams& p) {                                                \
+  bool NAME(int D, int G, int tiles, bool loop, bool heads, int nw, dim3 grid,      \
+            hipStream_t s, const DecodeParams& p) {                                 \
     switch ((D * 32 + G) * 4 + tiles) {                                             \
       PA_MFMA_CASE(DT, 64, 8, 1) PA_MFMA_CASE(DT, 64, 8, 2)                         \
       PA_MFMA_CASE(DT, 128, 8, 1) PA_MFMA_CASE(DT, 128, 8, 2)                       \

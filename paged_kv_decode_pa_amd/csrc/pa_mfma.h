@@ -124,7 +124,13 @@ __device__ __forceinline__ bool any_rescale(float alpha) {
 template <int D>
 constexpr int acc_stride() { return D + 4; }
 
-template <int DT, int D, int G, int TILES, bool LOOP>
+// HEADS: one wavefront per KV head (the workgroup holds Hkv wavefronts and
+// one (sequence, partition) unit for all heads), each walking every chunk of
+// its head and writing its own rows; otherwise the workgroup's wavefronts
+// split one head's chunks and merge in LDS.  A token's rows of all KV heads
+// are adjacent in memory: with HEADS they are fetched by one workgroup (one
+// XCD) at about the same time.
+template <int DT, int D, int G, int TILES, bool LOOP, bool HEADS = false>
 __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParams p) {
   using S = MfmaShape<DT, D, G, TILES>;
   constexpr int NT = S::NT, KS = S::KS, MT = S::MT, VLOADS = S::VLOADS;
@@ -141,7 +147,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
   char* vbuf = reinterpret_cast<char*>(s_wave);
   int32_t* tbl = reinterpret_cast<int32_t*>(s_wave + S::TBL);
 
-  for_units<DT, D, G, LOOP>(p, [&](const Unit& u) {
+  // the chunks of a unit this wavefront takes: w, w + nw, ... (all of them
+  // with HEADS)
+  const int cw = HEADS ? 0 : w;
+  const int cstride = HEADS ? 1 : nw;
+
+  for_units<DT, D, G, LOOP, HEADS>(p, [&](const Unit& u) {
   const int Hq = p.num_heads;
   const int b = u.b, g = u.g, lo = u.lo, hi = u.hi;
 
@@ -345,7 +356,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
   uint4 kf0[TILES][KS], kf1[TILES][KS];
   char* vb0 = vbuf;
   char* vb1 = vbuf + S::VBYTES;
-  int c = c0 + w;
+  int c = c0 + cw;
   if (c <= c1) {
     Addr a;
     addr_of(c, a);
@@ -353,21 +364,51 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
     __builtin_amdgcn_sched_barrier(0);
     vcopy(a, vb0);
     __builtin_amdgcn_sched_barrier(0);
-    addr_of(c + nw, a);
+    addr_of(c + cstride, a);
     issue_k(a, kf1);
     __builtin_amdgcn_sched_barrier(0);
     vcopy(a, vb1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma clang loop unroll(disable)
-    for (; c <= c1; c += 2 * nw) {
-      step(c, c + 2 * nw, kf0, vb0);
-      step(c + nw, c + 3 * nw, kf1, vb1);
+    for (; c <= c1; c += 2 * cstride) {
+      step(c, c + 2 * cstride, kf0, vb0);
+      step(c + cstride, c + 3 * cstride, kf1, vb1);
     }
   }
   // drain the trailing loads before the wavefront moves on
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
+
+  if constexpr (HEADS) {
+    // this wavefront holds its head's whole unit: write from registers
+    float l = l_run;
+    l += shfl_xor_f(l, 16);
+    l += shfl_xor_f(l, 32);
+    if (c16 < G) {
+      const float inv = 1.0f / l;
+      const size_t row = (size_t)b * Hq + (size_t)g * G + c16;
+      if (u.single) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const uint2 v = make_uint2(pack2<DT>(acc[mt][0] * inv, acc[mt][1] * inv),
+                                     pack2<DT>(acc[mt][2] * inv, acc[mt][3] * inv));
+          *reinterpret_cast<uint2*>(static_cast<char*>(p.out) + (row * D + 16 * mt + 4 * j) * EB) =
+              v;
+        }
+      } else {
+        const size_t pi = row * p.num_parts + u.part;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          *reinterpret_cast<f32x4_t*>(p.tmp_out + pi * D + 16 * mt + 4 * j) = acc[mt] * inv;
+        if (j == 0) {
+          p.max_logits[pi] = m_run;
+          p.exp_sums[pi] = l;
+        }
+      }
+    }
+    return;
+  }
 
   // ---- epilogue: sums over the head's four lanes, then the LDS merge ----
   l_run += shfl_xor_f(l_run, 16);
