@@ -556,14 +556,22 @@ int pa_mq_attention(void* out, void* workspace, size_t workspace_bytes, const vo
                : pa::launch_mq_wg_bf16(head_dim, nr, tiles_per_chunk, nbuf, grid, s, p);
     } else {
       const int tiles_per_chunk = block_size >= 32 && nr * head_dim <= 128 ? 2 : 1;
-      const size_t lds_wave = pa::mq_mfma_lds_bytes(head_dim, nr, tiles_per_chunk);
+      // one wavefront per KV head when the heads' LDS fits two workgroups
+      // per CU (PA_MQ_HEADS=0 switches it off)
+      const size_t lds_heads = pa::mq_mfma_lds_bytes(head_dim, nr, tiles_per_chunk, true);
+      const bool heads = num_kv_heads <= pa::kMaxWaves &&
+                         (size_t)num_kv_heads * lds_heads <= 80 * 1024 &&
+                         env_int("PA_MQ_HEADS", 1) != 0;
+      const size_t lds_wave = pa::mq_mfma_lds_bytes(head_dim, nr, tiles_per_chunk, false);
       const int span = window > 0 && window < p.part ? window : p.part;
-      int nw = waves_for(span, 16 * tiles_per_chunk,
-                         (int)(blocks < (1L << 30) ? blocks : (1L << 30)));
-      while (nw > 1 && nw * lds_wave > PA_WG_LDS_CAP) nw /= 2;
+      int nw = heads ? num_kv_heads
+                     : waves_for(span, 16 * tiles_per_chunk,
+                                 (int)(blocks < (1L << 30) ? blocks : (1L << 30)));
+      while (!heads && nw > 1 && nw * lds_wave > PA_WG_LDS_CAP) nw /= 2;
+      const dim3 g_grid((unsigned)(heads ? blocks / num_kv_heads : blocks));
       ok = dtype == PA_F16
-               ? pa::launch_mq_mfma_f16(head_dim, nr, tiles_per_chunk, nw, grid, s, p)
-               : pa::launch_mq_mfma_bf16(head_dim, nr, tiles_per_chunk, nw, grid, s, p);
+               ? pa::launch_mq_mfma_f16(head_dim, nr, tiles_per_chunk, heads, nw, g_grid, s, p)
+               : pa::launch_mq_mfma_bf16(head_dim, nr, tiles_per_chunk, heads, nw, g_grid, s, p);
     }
     if (!ok) return PA_EUNSUPPORTED;
     rc = hipGetLastError() == hipSuccess ? PA_OK : PA_ELAUNCH;

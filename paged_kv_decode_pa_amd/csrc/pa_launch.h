@@ -25,11 +25,12 @@ size_t decode_mfma_lds_bytes(int D, int G, int tiles);
 
 // Tiled multi-query path (f16/bf16, block_size >= 16 * tiles); nr 16-row
 // blocks per wavefront.  Returns false when not built for the shape.
-bool launch_mq_mfma_f16(int D, int nr, int tiles, int nw, dim3 grid, hipStream_t s,
+// heads: one wavefront per KV head (nw = num_kv_heads).
+bool launch_mq_mfma_f16(int D, int nr, int tiles, bool heads, int nw, dim3 grid, hipStream_t s,
                         const MQParams& p);
-bool launch_mq_mfma_bf16(int D, int nr, int tiles, int nw, dim3 grid, hipStream_t s,
+bool launch_mq_mfma_bf16(int D, int nr, int tiles, bool heads, int nw, dim3 grid, hipStream_t s,
                          const MQParams& p);
-size_t mq_mfma_lds_bytes(int D, int nr, int tiles);
+size_t mq_mfma_lds_bytes(int D, int nr, int tiles, bool heads);
 
 // Workgroup-shared multi-query path (four wavefronts of 16 * nr rows each).
 bool launch_mq_wg_f16(int D, int nr, int tiles, int nbuf, dim3 grid, hipStream_t s,
@@ -93,8 +94,13 @@ bool launch_mq_wg_bf16(int D, int nr, int tiles, int nbuf, dim3 grid, hipStream_
 
 #define PA_MQ_CASE(DT, DV, NRV, TV)                                                 \
   case (DV * 8 + NRV) * 4 + TV: {                                                   \
-    const size_t lds = (size_t)nw * sizeof(float) * MQShape<DT, DV, NRV, TV>::LDS_FLOATS; \
-    mq_mfma_kernel<DT, DV, NRV, TV><<<grid, dim3(64 * nw), lds, s>>>(p);             \
+    if (heads) {                                                                    \
+      const size_t lds = (size_t)nw * sizeof(float) * MQShape<DT, DV, NRV, TV, true>::LDS_FLOATS; \
+      mq_mfma_kernel<DT, DV, NRV, TV, true><<<grid, dim3(64 * nw), lds, s>>>(p);     \
+    } else {                                                                        \
+      const size_t lds = (size_t)nw * sizeof(float) * MQShape<DT, DV, NRV, TV>::LDS_FLOATS; \
+      mq_mfma_kernel<DT, DV, NRV, TV><<<grid, dim3(64 * nw), lds, s>>>(p);           \
+    }                                                                               \
     return true;                                                                    \
   }
 
@@ -102,7 +108,8 @@ bool launch_mq_wg_bf16(int D, int nr, int tiles, int nbuf, dim3 grid, hipStream_
 // chunks only while nr * head_dim <= 128 (the accumulators, query and K
 // fragments stay in registers)
 #define PA_DEFINE_MQ_LAUNCHER(NAME, DT)                                             \
-  bool NAME(int D, int nr, int tiles, int nw, dim3 grid, hipStream_t s, const MQParams& p) { \
+  bool NAME(int D, int nr, int tiles, bool heads, int nw, dim3 grid, hipStream_t s,  \
+            const MQParams& p) {                                                    \
     switch ((D * 8 + nr) * 4 + tiles) {                                             \
       PA_MQ_CASE(DT, 64, 1, 1) PA_MQ_CASE(DT, 64, 1, 2)                             \
       PA_MQ_CASE(DT, 64, 2, 1) PA_MQ_CASE(DT, 64, 2, 2)                             \

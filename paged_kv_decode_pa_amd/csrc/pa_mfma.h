@@ -17,9 +17,9 @@
 //           the K index is valid); A = V transposed, gathered from LDS.
 //   The accumulators are rescaled only in chunks where some head's running
 //   maximum moved.
-//   Two chunks are in flight per wavefront: K in two register slots, V in
-//   two LDS buffers.  V is copied HBM -> LDS by the buffer unit (direct-to-LDS 16-byte loads,
-//   no registers in between).  Within a row the 16-byte segments are stored
+//   PA_MFMA_DEPTH (2) chunks are in flight per wavefront: K in register
+//   slots, V in LDS buffers.  V is copied HBM -> LDS by the buffer unit
+//   (direct-to-LDS 16-byte loads, no registers in between).  Within a row the 16-byte segments are stored
 //   XOR-swizzled (v_swz), so a transposed read hits distinct LDS banks.
 #pragma once
 
@@ -67,6 +67,13 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// Chunks in flight per wavefront.  Measured on the long-context workload:
+// 2 -> 153 us, 3 -> 160 us, 4 -> 175 us (each extra V buffer costs LDS and
+// each K slot registers, and fewer wavefronts fit).
+#ifndef PA_MFMA_DEPTH
+#define PA_MFMA_DEPTH 2
+#endif
+
 template <int DT, int D, int G, int TILES>
 struct MfmaShape {
   static constexpr int NT = 16 * TILES;             // tokens per chunk
@@ -74,8 +81,9 @@ struct MfmaShape {
   static constexpr int MT = D / 16;                 // P.V tiles over head_dim
   static constexpr int VBYTES = NT * D * 2;         // V chunk in LDS
   static constexpr int VLOADS = VBYTES / 1024;      // 1 KB direct-to-LDS loads
-  // LDS floats per wavefront: two V chunks, block-table window, max/sum, acc
-  static constexpr int V_F = 2 * VBYTES / 4;
+  static constexpr int DEPTH = PA_MFMA_DEPTH;       // chunks in flight per wavefront
+  // LDS floats per wavefront: DEPTH V chunks, block-table window, max/sum, acc
+  static constexpr int V_F = DEPTH * VBYTES / 4;
   static constexpr int TBL = V_F;
   static constexpr int ML = TBL + 64;
   static constexpr int ACC = ML + 2 * G;
@@ -262,7 +270,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
   };
 
   // One chunk cc: q.k on the K slot, then that slot and V buffer `vb` are
-  // refilled with chunk cn (a few bytes of q past the last chunk), so two
+  // refilled with chunk cn (a few bytes of q past the last chunk), so DEPTH
   // chunks stay in flight while this one is computed.  A chunk past the end
   // is fully masked and leaves the running state unchanged.
   auto step = [&](int cc, int cn, uint4 (&k)[TILES][KS], char* vb) {
@@ -332,7 +340,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
     // O^T += V^T . P^T, V^T gathered from LDS in the same token order.
     // Issued after this chunk's V copy: the other slot's K and V, and the K
     // just issued.
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * NK + NV));
+    __builtin_amdgcn_s_waitcnt(vmcnt_only((S::DEPTH - 1) * (NK + NV) + NK));
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -353,26 +361,24 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  uint4 kf0[TILES][KS], kf1[TILES][KS];
-  char* vb0 = vbuf;
-  char* vb1 = vbuf + S::VBYTES;
+  constexpr int DEPTH = S::DEPTH;
+  uint4 kf[DEPTH][TILES][KS];
   int c = c0 + cw;
   if (c <= c1) {
-    Addr a;
-    addr_of(c, a);
-    issue_k(a, kf0);
-    __builtin_amdgcn_sched_barrier(0);
-    vcopy(a, vb0);
-    __builtin_amdgcn_sched_barrier(0);
-    addr_of(c + cstride, a);
-    issue_k(a, kf1);
-    __builtin_amdgcn_sched_barrier(0);
-    vcopy(a, vb1);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) {
+      Addr a;
+      addr_of(c + i * cstride, a);
+      issue_k(a, kf[i]);
+      __builtin_amdgcn_sched_barrier(0);
+      vcopy(a, vbuf + i * S::VBYTES);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma clang loop unroll(disable)
-    for (; c <= c1; c += 2 * cstride) {
-      step(c, c + 2 * cstride, kf0, vb0);
-      step(c + cstride, c + 3 * cstride, kf1, vb1);
+    for (; c <= c1; c += DEPTH * cstride) {
+#pragma unroll
+      for (int i = 0; i < DEPTH; ++i)
+        step(c + i * cstride, c + (i + DEPTH) * cstride, kf[i], vbuf + i * S::VBYTES);
     }
   }
   // drain the trailing loads before the wavefront moves on

@@ -58,7 +58,7 @@ struct MQParams {
   float cap_mul;
 };
 
-template <int DT, int D, int NR, int TILES>
+template <int DT, int D, int NR, int TILES, bool HEADS = false>
 struct MQShape {
   static constexpr int R = 16 * NR;             // rows per wavefront
   static constexpr int NT = 16 * TILES;         // tokens per chunk
@@ -66,19 +66,24 @@ struct MQShape {
   static constexpr int MT = D / 16;             // P.V tiles over head_dim
   static constexpr int VBYTES = NT * D * 2;     // V chunk in LDS
   static constexpr int VLOADS = VBYTES / 1024;  // 1 KB direct-to-LDS loads
-  // LDS floats per wavefront: the two V chunks (after the loop: the [R][D]
-  // accumulators, rows padded to D + 4), the block-table window, max and sum
-  // per row
-  static constexpr int BUF = (2 * VBYTES / 4 > R * (D + 4)) ? 2 * VBYTES / 4 : R * (D + 4);
+  // LDS floats per wavefront: the two V chunks (after the loop, unless
+  // HEADS: the [R][D] accumulators, rows padded to D + 4), the block-table
+  // window, max and sum per row
+  static constexpr int BUF = (HEADS || 2 * VBYTES / 4 > R * (D + 4)) ? 2 * VBYTES / 4 : R * (D + 4);
   static constexpr int TBL = BUF;
   static constexpr int ML = TBL + 64;
   static constexpr int LDS_FLOATS = ML + 2 * R;
   static_assert(VBYTES % 1024 == 0, "chunk must fill whole 1 KB LDS loads");
 };
 
-template <int DT, int D, int NR, int TILES>
+// HEADS: one wavefront per KV head, the workgroup holding one (tile,
+// partition) unit for every head (a token's rows of all heads are adjacent in
+// memory and get fetched together); each wavefront walks all chunks of its
+// head and writes its rows from registers.  Otherwise the wavefronts split
+// one head's chunks and merge in LDS.
+template <int DT, int D, int NR, int TILES, bool HEADS = false>
 __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
-  using S = MQShape<DT, D, NR, TILES>;
+  using S = MQShape<DT, D, NR, TILES, HEADS>;
   constexpr int R = S::R, NT = S::NT, KS = S::KS, MT = S::MT, VLOADS = S::VLOADS;
   constexpr int EB = 2;
   typedef const __attribute__((address_space(4))) int32_t cint32;
@@ -95,12 +100,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
   char* vbuf = reinterpret_cast<char*>(s_wave);
   int32_t* tbl = reinterpret_cast<int32_t*>(s_wave + S::TBL);
 
-  // unit: KV head fastest, then tiles (a sequence's tiles side by side, so
-  // they share its pages in L2), then partitions
+  // unit: KV head fastest (or the wavefront's head), then tiles (a
+  // sequence's tiles side by side, so they share its pages in L2), then
+  // partitions
   const int Hq = p.num_heads;
   const int G = p.group;
-  const int g = blockIdx.x % p.num_kv_heads;
-  const int rest = blockIdx.x / p.num_kv_heads;
+  const int g = HEADS ? w : (int)(blockIdx.x % p.num_kv_heads);
+  const int rest = HEADS ? (int)blockIdx.x : (int)(blockIdx.x / p.num_kv_heads);
+  const int cw = HEADS ? 0 : w;       // first chunk of this wavefront
+  const int cstride = HEADS ? 1 : nw;  // its chunk stride
   const int tile = rest % p.max_tiles;
   const int part = rest / p.max_tiles;
   if (tile >= *(cint32*)p.num_tiles) return;
@@ -339,7 +347,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
   uint4 kf0[TILES][KS], kf1[TILES][KS];
   char* vb0 = vbuf;
   char* vb1 = vbuf + S::VBYTES;
-  int c = c0 + w;
+  int c = c0 + cw;
   if (c <= c1) {
     Addr a;
     addr_of(c, a);
@@ -347,15 +355,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
     __builtin_amdgcn_sched_barrier(0);
     vcopy(a, vb0);
     __builtin_amdgcn_sched_barrier(0);
-    addr_of(c + nw, a);
+    addr_of(c + cstride, a);
     issue_k(a, kf1);
     __builtin_amdgcn_sched_barrier(0);
     vcopy(a, vb1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma clang loop unroll(disable)
-    for (; c <= c1; c += 2 * nw) {
-      step(c, c + 2 * nw, kf0, vb0);
-      step(c + nw, c + 3 * nw, kf1, vb1);
+    for (; c <= c1; c += 2 * cstride) {
+      step(c, c + 2 * cstride, kf0, vb0);
+      step(c + cstride, c + 3 * cstride, kf1, vb1);
     }
   }
   // drain the trailing loads (the V buffers are reused below)
@@ -363,6 +371,42 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  if constexpr (HEADS) {
+    // the wavefront holds its head's whole unit: write its rows directly
+#pragma unroll
+    for (int nb = 0; nb < NR; ++nb) {
+      float l = l_run[nb];
+      l += shfl_xor_f(l, 16);
+      l += shfl_xor_f(l, 32);
+      const int f = f0 + 16 * nb + c16;
+      if (f >= f_end || l == 0.0f) continue;  // past the end, or no key here
+      const float inv = 1.0f / l;
+      const int i = f / G;
+      const int h = f - i * G;
+      const int pos = L - n + i;
+      const size_t row = (size_t)(q0 + i) * Hq + (size_t)g * G + h;
+      if (key_lo(pos) / P == pos / P) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const size_t e = row * D + 16 * mt + 4 * j;
+          const uint2 v = make_uint2(pack2<DT>(acc[nb][mt][0] * inv, acc[nb][mt][1] * inv),
+                                     pack2<DT>(acc[nb][mt][2] * inv, acc[nb][mt][3] * inv));
+          *reinterpret_cast<uint2*>(static_cast<char*>(p.out) + e * EB) = v;
+        }
+      } else {
+        const size_t pi = row * p.num_parts + part;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          *reinterpret_cast<f32x4_t*>(p.tmp_out + pi * D + 16 * mt + 4 * j) = acc[nb][mt] * inv;
+        if (j == 0) {
+          p.max_logits[pi] = m_run[nb];
+          p.exp_sums[pi] = l;
+        }
+      }
+    }
+    return;
+  }
 
   // ---- epilogue: per-row sums over the four lanes, staged in LDS ----
   float* s_acc = s_wave;
