@@ -55,6 +55,7 @@ struct DecodeParams {
   int num_parts;           // NP
   float qk_mul;            // multiplies q.k
   float cap_mul;           // > 0: logit2 = cap_mul * tanh(q.k * qk_mul)
+  int xcd_units;           // > 0: XCD-grouped grid over this many (b, p) units
 };
 
 struct ReduceParams {
@@ -130,12 +131,27 @@ __device__ __forceinline__ bool unit_range(const DecodeParams& p, Unit& u) {
 // longest-first order, then partitions (so a sequence's partitions are
 // spread over the whole dispatch).  HEADS: the workgroup holds every KV head
 // of its (sequence, partition), wavefront w taking head w.
+//
+// XCD grouping (xcd_units > 0): workgroups are handed to the eight XCDs in
+// turn (workgroup i to XCD i mod 8), so workgroup i is read as slot i / 8 of
+// XCD i mod 8, and the KV heads of one (sequence, partition) take
+// consecutive slots of the same XCD: a token's rows of all heads (adjacent
+// in memory) are then fetched through one L2.  The grid is padded to a
+// multiple of 8 * Hkv; padding workgroups have no unit.
 template <int DT, int D, int G, bool HEADS = false>
 __device__ __forceinline__ bool grid_unit(const DecodeParams& p, Unit& u) {
   typedef const __attribute__((address_space(4))) int32_t cint32;
   const int id = blockIdx.x;
-  u.g = HEADS ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : id % p.num_kv_heads;
-  const int rest = HEADS ? id : id / p.num_kv_heads;
+  int rest;
+  if (!HEADS && p.xcd_units > 0) {
+    const int slot = id >> 3;
+    u.g = slot % p.num_kv_heads;
+    rest = (slot / p.num_kv_heads) * 8 + (id & 7);
+    if (rest >= p.xcd_units) return false;
+  } else {
+    u.g = HEADS ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : id % p.num_kv_heads;
+    rest = HEADS ? id : id / p.num_kv_heads;
+  }
   u.part = rest / p.num_seqs;
   u.b = p.order ? ((cint32*)p.order)[rest % p.num_seqs] : rest % p.num_seqs;
   return unit_range<DT, D, G, HEADS>(p, u);
