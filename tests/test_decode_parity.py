@@ -123,27 +123,40 @@ MFMA_SHAPES = [
 ]
 
 
+# path -> environment: the matrix-core kernel with one wavefront per KV head
+# (default) or with wavefronts splitting one head's chunks, and the vector
+# kernel with and without the XCD-grouped grid
+GROUP_PATHS = {
+    "mfma-heads": {"PA_DECODE_MFMA": "1", "PA_DECODE_HEADS": "1"},
+    "mfma-split": {"PA_DECODE_MFMA": "1", "PA_DECODE_HEADS": "0"},
+    "valu-xcd": {"PA_DECODE_MFMA": "0", "PA_DECODE_XCD": "1"},
+    "valu-plain": {"PA_DECODE_MFMA": "0", "PA_DECODE_XCD": "0"},
+}
+
+
 @pytest.mark.parametrize("shape", MFMA_SHAPES,
                          ids=[f"{s[0]}-g{s[1]//s[2]}-d{s[3]}-bs{s[4]}-c{s[5]:g}-w{s[6]}-p{s[7]}" for s in MFMA_SHAPES])
-@pytest.mark.parametrize("path", ["mfma", "valu"])
+@pytest.mark.parametrize("path", list(GROUP_PATHS))
 def test_group_path_shapes(shape, path):
     import os
     from gpu_util import say
     dt, Hq, Hkv, D, bs, cap, W, P = shape
     G = Hq // Hkv
-    if path == "valu" and G > 8:
+    if path.startswith("valu") and G > 8:
         pytest.skip("the vector path takes groups of up to 8 heads")
     say(f"group path {path} {shape}")
     L = [1, 5, 33, 200, 700, 64, 1000]
     c = make_case(B=len(L), Hq=Hq, Hkv=Hkv, D=D, bs=bs, dtype=dt, context_lens=L,
                   softcap=cap, window=W, partition_size=P, seed=sum(map(ord, str(shape))) + 7,
                   extra_table_cols=2)
-    os.environ["PA_DECODE_MFMA"] = "1" if path == "mfma" else "0"
+    env = GROUP_PATHS[path]
+    os.environ.update(env)
     try:
         for waves in (1, 4):
             check(c, gpu(c, waves=waves))
     finally:
-        os.environ.pop("PA_DECODE_MFMA", None)
+        for k in env:
+            os.environ.pop(k, None)
 
 
 def test_looping_launch_over_many_partitions():

@@ -36,16 +36,20 @@ class DeviceMQ:
             self.value = upload(c.value, c.dtype)
             self.slots = torch.from_numpy(c.slot_mapping).cuda()
 
-    def run(self, partition_size=None, tiled=None, out=None, max_query_len=None, shared=None):
+    def run(self, partition_size=None, tiled=None, out=None, max_query_len=None, shared=None,
+            env=None):
         """tiled: matrix-core path (True) or per token (False); shared: force
-        the workgroup-shared (True) or per-wavefront (False) tiled kernel."""
+        the workgroup-shared (True) or per-wavefront (False) tiled kernel;
+        env: further switches for this call."""
         import torch
         import paged_kv_decode_pa_amd as pa
         c = self.c
+        env = dict(env or {})
         if tiled is not None:
-            os.environ["PA_MQ_TILED"] = "1" if tiled else "0"
+            env["PA_MQ_TILED"] = "1" if tiled else "0"
         if shared is not None:
-            os.environ["PA_MQ_WG"] = "1" if shared else "0"
+            env["PA_MQ_WG"] = "1" if shared else "0"
+        os.environ.update(env)
         try:
             if self.slots is not None:
                 pa.reshape_and_cache(self.key, self.value, self.k_cache, self.v_cache, self.slots)
@@ -56,8 +60,8 @@ class DeviceMQ:
                                   max_query_len=max_query_len or max(1, c.max_query_len), out=out)
             torch.cuda.synchronize()
         finally:
-            os.environ.pop("PA_MQ_TILED", None)
-            os.environ.pop("PA_MQ_WG", None)
+            for k in env:
+                os.environ.pop(k, None)
         return out
 
 
@@ -91,8 +95,11 @@ def _id(s):
     return f"{s[0]}-g{s[1]}-d{s[2]}-bs{s[3]}-c{int(s[4])}-w{s[5]}-p{s[6]}"
 
 
-PATHS = {"shared": (True, True), "wave": (True, False), "auto": (True, None),
-         "pertoken": (False, None)}
+# path -> (tiled, shared, extra switches): the per-wavefront kernel runs with
+# one wavefront per KV head by default ("wave") or split chunks ("wave-split")
+PATHS = {"shared": (True, True, None), "wave": (True, False, None),
+         "wave-split": (True, False, {"PA_MQ_HEADS": "0"}), "auto": (True, None, None),
+         "pertoken": (False, None, None)}
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=[_id(s) for s in SHAPES])
@@ -100,7 +107,7 @@ PATHS = {"shared": (True, True), "wave": (True, False), "auto": (True, None),
 def test_mq_shapes(shape, path):
     from gpu_util import say
     dtype, G, D, bs, cap, W, P, L, n = shape
-    tiled, shared = PATHS[path]
+    tiled, shared, env = PATHS[path]
     if not tiled and G not in (1, 2, 4, 8, 16):
         pytest.skip("the per-token path takes the decode group sizes")
     say(f"mq {_id(shape)} path={path}")
@@ -108,7 +115,7 @@ def test_mq_shapes(shape, path):
     c = make_mq_case(Hq=G * Hkv, Hkv=Hkv, D=D, bs=bs, dtype=dtype, context_lens=L, query_lens=n,
                      softcap=cap, window=W, partition_size=P, seed=D + G + bs + W,
                      new_rows=True)
-    got = DeviceMQ(c).run(tiled=tiled, shared=shared)
+    got = DeviceMQ(c).run(tiled=tiled, shared=shared, env=env)
     check(got, oracle.multi_query_case(c), dtype)
 
 
