@@ -133,11 +133,10 @@ __device__ __forceinline__ void widen16<DT_F32>(const uint4& v, float* o) {
 // ---------------------------------------------------------------------------
 // float32 -> storage type, round to nearest even
 // ---------------------------------------------------------------------------
+// float -> bf16 with round-to-nearest-even: gfx950 converts in hardware
+// (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)(0x7fc0u | ((u >> 16) & 0x8000u));
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (_Float16)x);

@@ -58,9 +58,9 @@ __device__ __forceinline__ f32x4_t mfma_k16(const uint2& a, const uint2& b, f32x
 template <int DT>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   if constexpr (DT == DT_F16)
-    return (uint32_t)f32_to_f16_bits(lo) | ((uint32_t)f32_to_f16_bits(hi) << 16);
+    return __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)lo, (_Float16)hi});
   else
-    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+    return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)lo, (__bf16)hi});
 }
 
 // s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding:
@@ -302,14 +302,19 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
 #pragma unroll
         for (int i = 0; i < 4; ++i) pr[t][i] = sc[t][i] * p.qk_mul;
     }
+    if (cs < lo || cs + NT > hi) {  // only a unit's first and last chunks need the mask
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pos = cs + 16 * t + 4 * j + i;
+          pr[t][i] = (pos >= lo && pos < hi) ? pr[t][i] : kNegInf;
+        }
+    }
 #pragma unroll
     for (int t = 0; t < TILES; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pos = cs + 16 * t + 4 * j + i;
-        pr[t][i] = (pos >= lo && pos < hi) ? pr[t][i] : kNegInf;
-        cmax = fmaxf(cmax, pr[t][i]);
-      }
+      for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, pr[t][i]);
     cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
     cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
     const float m_new = fmaxf(m_run, cmax);

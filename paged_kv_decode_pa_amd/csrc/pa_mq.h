@@ -150,6 +150,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
       qf[nb][s] = act ? ld16(qb + (size_t)s * 32 * EB) : make_uint4(0, 0, 0, 0);
   }
 
+  // keys every active row attends to: chunks inside need no mask (rows past
+  // the sequence's end are never written, whatever they accumulate)
+  const int full_lo = max(lo, key_lo(L - n + (min(f0 + R, f_end) - 1) / G));
+  const int full_hi = min(hi, L - n + f0 / G + 1);
+
   const int32_t* bt = p.block_tables + (size_t)b * p.max_blocks_per_seq;
   const int log2_bs = p.log2_bs;
   const int last_pg = (hi - 1) >> log2_bs;
@@ -284,14 +289,19 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
           for (int i = 0; i < 4; ++i) pr[t][i] = sc[nb][t][i] * p.qk_mul;
       }
       float cmax = kNegInf;
+      if (cs < full_lo || cs + NT > full_hi) {  // keys some row of the wavefront must not see
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int pos = cs + 16 * t + 4 * j + i;
+            pr[t][i] = (pos >= a_lo[nb] && pos < a_hi[nb]) ? pr[t][i] : kNegInf;
+          }
+      }
 #pragma unroll
       for (int t = 0; t < TILES; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int pos = cs + 16 * t + 4 * j + i;
-          pr[t][i] = (pos >= a_lo[nb] && pos < a_hi[nb]) ? pr[t][i] : kNegInf;
-          cmax = fmaxf(cmax, pr[t][i]);
-        }
+        for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, pr[t][i]);
       cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
       cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
       const float m_new = fmaxf(m_run[nb], cmax);
@@ -554,12 +564,15 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
     for (int s = 0; s < KS; ++s)
       qf[nb][s] = act ? ld16(qb + (size_t)s * 32 * EB) : make_uint4(0, 0, 0, 0);
   }
-  // keys this wavefront attends to at all (empty when it has no rows)
-  int wlo = hi, whi = lo;
+  // keys this wavefront attends to at all (empty when it has no rows), and
+  // keys all its rows attend to (chunks inside need no mask)
+  int wlo = hi, whi = lo, full_lo = hi, full_hi = lo;
   if (fw0 < f_end) {
     const int fl = min(fw0 + RW, f_end) - 1;
     wlo = max(lo, key_lo(L - n + fw0 / G));
     whi = min(hi, L - n + fl / G + 1);
+    full_lo = max(lo, key_lo(L - n + fl / G));
+    full_hi = min(hi, L - n + fw0 / G + 1);
   }
 
   const int32_t* bt = p.block_tables + (size_t)b * p.max_blocks_per_seq;
@@ -687,14 +700,19 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
           for (int i = 0; i < 4; ++i) pr[t][i] = sc[nb][t][i] * p.qk_mul;
       }
       float cmax = kNegInf;
+      if (cs < full_lo || cs + NT > full_hi) {  // keys some row of the wavefront must not see
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int pos = cs + 16 * t + 4 * j + i;
+            pr[t][i] = (pos >= a_lo[nb] && pos < a_hi[nb]) ? pr[t][i] : kNegInf;
+          }
+      }
 #pragma unroll
       for (int t = 0; t < TILES; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int pos = cs + 16 * t + 4 * j + i;
-          pr[t][i] = (pos >= a_lo[nb] && pos < a_hi[nb]) ? pr[t][i] : kNegInf;
-          cmax = fmaxf(cmax, pr[t][i]);
-        }
+        for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, pr[t][i]);
       cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
       cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
       const float m_new = fmaxf(m_run[nb], cmax);
