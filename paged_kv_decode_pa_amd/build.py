@@ -28,6 +28,10 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
     # device code: no packed FP32 arithmetic (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: the online-softmax rescale
+    # then multiplies them in place instead of copying them out of and back
+    # into accumulation registers (measured: prefill 227 -> 190 us)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
 
