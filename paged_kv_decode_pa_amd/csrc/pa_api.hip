@@ -422,7 +422,7 @@ int pa_mq_partition_size(int num_seqs, int num_tokens, int max_query_len, int nu
   if (mq_tiled(dtype, block_size, max_query_len)) {
     int nr = mq_row_blocks(head_dim, G, max_query_len);
     const bool wg = (long)max_query_len * G > 16L * nr;
-    if (wg) nr = head_dim == 64 ? (nr < 2 ? nr : 2) : 1;
+    if (wg) nr = 1;
     const int R = wg ? 64 * nr : 16 * nr;
     units = mq_max_tiles(num_seqs, num_tokens, G, R) * num_kv_heads;
   } else {
@@ -500,10 +500,10 @@ int pa_mq_attention(void* out, void* workspace, size_t workspace_bytes, const vo
   const int wg_env = env_int("PA_MQ_WG", -1);
   const bool wg = tiled && (wg_env >= 0 ? wg_env != 0
                                         : (long)max_query_len * G > 16L * nr);
-  // the shared kernel keeps four row-wavefronts per SIMD resident: two row
-  // blocks at head_dim 64, one above (measured: a 2048-token prefill at
-  // head_dim 64 runs 1.6x faster with two blocks than with four)
-  if (wg && nr_env == 0) nr = head_dim == 64 ? (nr < 2 ? nr : 2) : 1;
+  // the shared kernel takes one row block per wavefront: more workgroups
+  // stay resident (measured on a 2048-token prefill at head_dim 64: 182 us
+  // with one block, 189 with two, 245 with four)
+  if (wg && nr_env == 0) nr = 1;
   const int R = wg ? 64 * nr : 16 * nr;
   pa::mq_plan_kernel<<<dim3(1), dim3(1024), 0, s>>>(
       query_start, context_lens, num_seqs, num_tokens, max_context_len, G, R,
