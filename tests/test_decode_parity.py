@@ -268,3 +268,18 @@ def test_output_guard_band_untouched():
     run_step(DeviceCase(c), out=out)
     assert torch.all(big[0] == 7.0) and torch.all(big[-1] == 7.0)
     check(c, out.float().cpu().numpy().astype(np.float64))
+
+
+@pytest.mark.parametrize("P", [0, 16])
+def test_many_sequences(P):
+    """More sequences than one plan slice (1,024), mixed lengths (the plan's
+    order and, with a split, its item list)."""
+    from gpu_util import say
+    say(f"many sequences P={P}")
+    rng = np.random.default_rng(91)
+    B = 3000
+    L = rng.integers(0, 60, size=B)
+    c = make_case(B=B, Hq=8, Hkv=2, D=64, bs=16, dtype="f16", context_lens=L, seed=92,
+                  partition_size=P, poison=False)
+    sample = sorted(set(rng.choice(B, size=60, replace=False).tolist()) | {int(np.argmax(L))})
+    check(c, gpu(c), seqs=sample)

@@ -230,3 +230,20 @@ def test_mq_workloads_sampled(name):
     got = DeviceMQ(c).run()
     toks, want = _sampled(c, 48, 7)
     check(got, want, c.dtype, rows=toks)
+
+
+def test_mq_many_sequences():
+    """More sequences than the plan stages in LDS (4,096) and than one plan
+    slice (1,024): every token still finds its sequence."""
+    from gpu_util import say
+    say("mq many sequences")
+    rng = np.random.default_rng(77)
+    B = 4500
+    L = rng.integers(1, 40, size=B)
+    n = np.minimum(L, rng.integers(0, 4, size=B))
+    c = make_mq_case(Hq=4, Hkv=2, D=64, bs=16, dtype="bf16", context_lens=L, query_lens=n,
+                     partition_size=0, seed=78, new_rows=True, poison=False)
+    for tiled, shared in ((True, False), (False, None)):
+        got = DeviceMQ(c).run(tiled=tiled, shared=shared)
+        toks, want = _sampled(c, 200, 5)
+        check(got, want, "bf16", rows=toks)
