@@ -116,6 +116,29 @@ def cpu_baseline(case, budget_s: float):
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}
 
 
+def cold_times(step_fn, reps: int, dev, flush_mib: int = 1024):
+    """Median event-timed step with the caches evicted first: before each rep
+    a 1 GiB scratch buffer is read (more than the 256 MB Infinity Cache and
+    the L2s), so the step's K/V come from HBM.  Returns (step_ms, attn_ms)
+    where step_fn(record) returns the (start, end) events of its attention
+    call, or None (then attn_ms is the step's)."""
+    import torch
+    scratch = torch.ones(flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    steps, attn = [], []
+    for _ in range(reps):
+        scratch.sum()  # evicts: reads 1 GiB
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        a = step_fn(True)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        steps.append(e0.elapsed_time(e1))
+        attn.append(a[0].elapsed_time(a[1]) if a is not None else steps[-1])
+    del scratch
+    return float(np.median(steps)), float(np.median(attn))
+
+
 def calibration_copy(mib: int, dev):
     """Three plain device copies of `mib` MiB: the yardstick that scales the
     FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -204,6 +227,7 @@ def bench_mq(args):
 
     def step(record=False):
         pa.reshape_and_cache(key, value, kc, vc, slots)
+        e = None
         if record:
             e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             e[0].record(stream)
@@ -212,7 +236,7 @@ def bench_mq(args):
                         workspace=ws)
         if record:
             e[1].record(stream)
-            ev.append(e)
+        return e
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -220,11 +244,12 @@ def bench_mq(args):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(record=True)
+        ev.append(step(record=True))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     attn_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    cold_step_ms, cold_attn_ms = cold_times(step, min(args.steps, 20), dev)
     print(f"[bench] timed {args.steps} steps: {ms_step*1e3:.1f} us/step wall, "
           f"pa_mq_attention {attn_ms*1e3:.1f} us (HIP events)", file=sys.stderr, flush=True)
     if args.calib_copy_mib:
@@ -295,6 +320,9 @@ def bench_mq(args):
         "algorithmic_bytes_per_step": ab["total"],
         "max_abs_err_vs_oracle": max_err,
         "roofline": roof,
+        "cold": {"step_us": round(cold_step_ms * 1e3, 2),
+                 "pa_mq_attention_us": round(cold_attn_ms * 1e3, 2),
+                 "note": "median over steps each preceded by reading a 1 GiB scratch buffer"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
@@ -361,11 +389,13 @@ def main():
     split = P > 0 and (maxL + P - 1) // P > 1
     stream = torch.cuda.current_stream()
 
-    ev = []  # (before, after) pa_decode, per timed step
+    ev = []  # (before, after) pa_decode, per step of the three-call loop
 
     def step(record=False):
+        """The three entry points in turn (events around pa_decode)."""
         if slots is not None:
             pa.reshape_and_cache(key, value, kc, vc, slots)
+        e = None
         if record:
             e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             e[0].record(stream)
@@ -373,27 +403,55 @@ def main():
                              case.window, P)
         if record:
             e[1].record(stream)
-            ev.append(e)
         if split:
             pa.decode_reduce(out, ws, cl, maxL, P, case.window)
+        return e
+
+    # the whole step as one native call (pa_step): preparation launch
+    # (new rows, plan, merge counters), decode, merge
+    fused = pa.Step(q, kc, vc, bt, cl, case.scale, case.softcap, case.window,
+                    partition_size=P, max_context_len=maxL, out=out, key=key, value=value,
+                    slot_mapping=slots)
+
+    def fused_step(record=False):
+        fused.run()
+        return None
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
+        fused_step()
         step()
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps; HIP events bracket each pa_decode launch
-    # on the stream it runs on (torch's current stream)
+    # timed region: exactly K steps of pa_step
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(record=True)
+        fused_step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
+    print(f"[bench] timed {args.steps} steps (pa_step): {ms_step*1e3:.1f} us/step wall",
+          file=sys.stderr, flush=True)
+
+    # the three entry points, K steps; HIP events bracket each pa_decode
+    # launch on the stream it runs on (torch's current stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        ev.append(step(record=True))
+    torch.cuda.synchronize()
+    ms_step3 = (time.perf_counter() - t0) * 1e3 / args.steps
     decode_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
-    print(f"[bench] timed {args.steps} steps: {ms_step*1e3:.1f} us/step wall, "
+    print(f"[bench] three calls: {ms_step3*1e3:.1f} us/step wall, "
           f"pa_decode {decode_ms*1e3:.1f} us (HIP events)", file=sys.stderr, flush=True)
+
+    reps = min(args.steps, 20)
+    cold_step_ms, _ = cold_times(fused_step, reps, dev)
+    cold_step3_ms, cold_decode_ms = cold_times(step, reps, dev)
+    print(f"[bench] cold (caches evicted before each step): pa_step {cold_step_ms*1e3:.1f} us, "
+          f"three calls {cold_step3_ms*1e3:.1f} us, pa_decode {cold_decode_ms*1e3:.1f} us",
+          file=sys.stderr, flush=True)
 
     # the same step captured once into a HIP graph and replayed K times
     graph = None
@@ -490,7 +548,15 @@ def main():
             "algorithmic_bytes_per_launch": ab["decode"],
             "kernel_sources": digest,
         },
+        "three_calls": {"ms_per_step": round(ms_step3, 5),
+                        "value": round(ab["total"] / (ms_step3 / 1e3) / 1e9, 2), "unit": "GB/s",
+                        "note": "reshape_and_cache, pa_decode, pa_decode_reduce as separate calls"},
         "graph_replay": graph,
+        "cold": {"step_us": round(cold_step_ms * 1e3, 2),
+                 "three_calls_step_us": round(cold_step3_ms * 1e3, 2),
+                 "pa_decode_us": round(cold_decode_ms * 1e3, 2),
+                 "pa_decode_gbs": round(ab["decode"] / (cold_decode_ms / 1e3) / 1e9, 2),
+                 "note": "median over steps each preceded by reading a 1 GiB scratch buffer"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

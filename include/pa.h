@@ -111,7 +111,10 @@ int pa_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads,
  * Bytes of workspace pa_decode needs (0 only when num_seqs <= 0):
  *   order      [num_seqs] int32, padded to 256 bytes: the sequences sorted
  *              longest first, written by pa_decode itself
- * and, when the keys are split (partition_size > 0 and NP > 1), after it:
+ *   count      one int32, padded to 256 bytes, and
+ *   items      [num_seqs * NP] int32 pairs, padded to 256 bytes: the
+ *              non-empty (sequence, partition) list of a looping launch
+ * and, when the keys are split (partition_size > 0 and NP > 1), after them:
  *   tmp_out    [num_seqs, num_heads, NP, head_dim] float32
  *   max_logits [num_seqs, num_heads, NP]           float32 (base-2 logits)
  *   exp_sums   [num_seqs, num_heads, NP]           float32
@@ -244,7 +247,14 @@ typedef struct {
   pa_dtype dtype;
 } pa_step_args;
 
-/* Runs the step on `stream` (no graph).  Returns the first failing status. */
+/*
+ * Runs the step on `stream` (no graph).  Returns the first failing status;
+ * argument errors are those of the three calls.  The results are those of
+ * the three calls in turn, bit for bit: one launch writes the new K/V rows
+ * and builds the sequence order (two launches in the three calls), then the
+ * decode kernel and (keys split) the reduce kernel run.  Environment
+ * PA_STEP_FUSE=0 makes it issue the three calls instead.
+ */
 int pa_step(const pa_step_args* args, void* stream);
 
 typedef struct pa_step_graph pa_step_graph; /* opaque */

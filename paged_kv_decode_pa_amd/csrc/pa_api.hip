@@ -138,8 +138,8 @@ int pa_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads, int 
   return part;
 }
 
-// Workspace layout, each part padded to 256 bytes: the plan (sequence order
-// [B] int32, item count, items [B*NP] int32 pairs), then, when the keys are
+// Workspace layout: the plan (sequence order [B] int32, item count, items
+// [B*NP] int32 pairs, each padded to 256 bytes), then, when the keys are
 // split, tmp_out [B,Hq,NP,D] f32, max_logits [B,Hq,NP] f32, exp_sums
 // [B,Hq,NP] f32.
 static size_t pad256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -165,14 +165,28 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim, int m
          partials_bytes(num_seqs, num_heads, head_dim, max_context_len, partition_size);
 }
 
-// pa_decode with an optional table-row map (multi-query launches run each
-// query token as a sequence of its own; see pa_mq_attention).
-static int decode_impl(void* out, void* workspace, size_t workspace_bytes, const void* q,
-                       const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                       int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
-                       int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
-                       int num_blocks, float scale, float softcap, int window, int partition_size,
-                       pa_dtype dtype, void* stream, const int32_t* seq_row) {
+// A checked pa_decode launch: the kernel parameters, the grid and whether
+// the plan kernel must run first.
+struct DecodeLaunch {
+  pa::DecodeParams p;
+  pa::Plan plan;
+  bool need_plan, mfma, heads, loop, paged;
+  int G, tiles, nw, head_dim;
+  pa_dtype dtype;
+  dim3 grid, block;
+};
+
+// Checks the arguments of pa_decode and makes its launch choices
+// (*empty: nothing to launch).  Multi-query launches pass a table-row map
+// (each query token runs as a sequence of its own; see pa_mq_attention).
+static int decode_setup(void* out, void* workspace, size_t workspace_bytes, const void* q,
+                        const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                        int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+                        int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                        int block_size, int num_blocks, float scale, float softcap, int window,
+                        int partition_size, pa_dtype dtype, const int32_t* seq_row,
+                        DecodeLaunch& dl, bool* empty) {
+  *empty = true;
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
       max_blocks_per_seq <= 0 || max_context_len < 0 || window < 0 || partition_size < 0)
     return PA_EINVAL;
@@ -190,6 +204,7 @@ static int decode_impl(void* out, void* workspace, size_t workspace_bytes, const
   if ((long)max_context_len > (long)max_blocks_per_seq * block_size) return PA_EINVAL;
   if (num_seqs == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_EINVAL;
+  *empty = false;
 
   const int np = num_parts(max_context_len, partition_size);
   const size_t need = pa_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
@@ -257,7 +272,6 @@ static int decode_impl(void* out, void* workspace, size_t workspace_bytes, const
   while (!heads && nw > 1 && nw * lds_wave > PA_WG_LDS_CAP) nw /= 2;
   const long blocks = (long)num_seqs * (heads ? 1 : num_kv_heads) * np;
   if (blocks > 0x7fffffffL) return PA_EUNSUPPORTED;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   // One workgroup per (sequence, KV head, partition), unless that grid is
   // more than twice what the chip holds at once and spans many partitions:
   // workgroups are dispatched at a bounded rate, so a grid of mostly empty
@@ -274,12 +288,7 @@ static int decode_impl(void* out, void* workspace, size_t workspace_bytes, const
   // PA_DECODE_PLAN=0/1 overrides.
   const int plan_env = env_int("PA_DECODE_PLAN", -1);
   const bool need_plan = loop || (plan_env >= 0 ? plan_env != 0 : num_seqs >= 48);
-  if (need_plan) {
-    pa::plan_kernel<<<dim3(1), dim3(1024), 0, s>>>(context_lens, num_seqs, max_context_len,
-                                                  window, p.part, plan);
-  } else {
-    p.order = nullptr;
-  }
+  if (!need_plan) p.order = nullptr;
   // XCD-grouped grid for per-head workgroups over split keys (measured: the
   // 16-sequence sliding-window workload 57 -> 52 us; the unsplit serving
   // batch loses 2.5 %, so it keeps the plain order).  PA_DECODE_XCD=0/1
@@ -294,23 +303,69 @@ static int decode_impl(void* out, void* workspace, size_t workspace_bytes, const
     const long per_round = 8L * num_kv_heads;
     grid_blocks = (blocks + per_round - 1) / per_round * per_round;
   }
-  const dim3 grid((unsigned)grid_blocks), block(64 * nw);
+  dl.p = p;
+  dl.plan = plan;
+  dl.need_plan = need_plan;
+  dl.mfma = mfma;
+  dl.heads = heads;
+  dl.loop = loop;
   // chunks of nt tokens stay inside one page when block_size >= nt
-  const bool paged = block_size >= nt;
+  dl.paged = block_size >= nt;
+  dl.G = G;
+  dl.tiles = tiles;
+  dl.nw = nw;
+  dl.head_dim = head_dim;
+  dl.dtype = dtype;
+  dl.grid = dim3((unsigned)grid_blocks);
+  dl.block = dim3(64 * nw);
+  return PA_OK;
+}
+
+// The decode kernel of a set-up launch (the plan, if needed, already queued).
+static int decode_kernel_launch(const DecodeLaunch& dl, hipStream_t s) {
+  const int D = dl.head_dim, G = dl.G;
   bool ok = false;
-  if (mfma) {
-    ok = dtype == PA_F16
-             ? pa::launch_decode_mfma_f16(head_dim, G, tiles, loop, heads, nw, grid, s, p)
-             : pa::launch_decode_mfma_bf16(head_dim, G, tiles, loop, heads, nw, grid, s, p);
+  if (dl.mfma) {
+    ok = dl.dtype == PA_F16
+             ? pa::launch_decode_mfma_f16(D, G, dl.tiles, dl.loop, dl.heads, dl.nw, dl.grid, s,
+                                          dl.p)
+             : pa::launch_decode_mfma_bf16(D, G, dl.tiles, dl.loop, dl.heads, dl.nw, dl.grid, s,
+                                           dl.p);
   } else {
-    switch (dtype) {
-      case PA_F32: ok = pa::launch_decode_f32(head_dim, G, paged, loop, grid, block, s, p); break;
-      case PA_F16: ok = pa::launch_decode_f16(head_dim, G, paged, loop, grid, block, s, p); break;
-      case PA_BF16: ok = pa::launch_decode_bf16(head_dim, G, paged, loop, grid, block, s, p); break;
+    switch (dl.dtype) {
+      case PA_F32:
+        ok = pa::launch_decode_f32(D, G, dl.paged, dl.loop, dl.grid, dl.block, s, dl.p);
+        break;
+      case PA_F16:
+        ok = pa::launch_decode_f16(D, G, dl.paged, dl.loop, dl.grid, dl.block, s, dl.p);
+        break;
+      case PA_BF16:
+        ok = pa::launch_decode_bf16(D, G, dl.paged, dl.loop, dl.grid, dl.block, s, dl.p);
+        break;
     }
   }
   if (!ok) return PA_EUNSUPPORTED;
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ELAUNCH;
+}
+
+static int decode_impl(void* out, void* workspace, size_t workspace_bytes, const void* q,
+                       const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                       int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+                       int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                       int num_blocks, float scale, float softcap, int window, int partition_size,
+                       pa_dtype dtype, void* stream, const int32_t* seq_row) {
+  DecodeLaunch dl;
+  bool empty = true;
+  const int st = decode_setup(out, workspace, workspace_bytes, q, k_cache, v_cache, block_tables,
+                              max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                              num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                              softcap, window, partition_size, dtype, seq_row, dl, &empty);
+  if (st != PA_OK || empty) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dl.need_plan)
+    pa::plan_kernel<<<dim3(1), dim3(1024), 0, s>>>(context_lens, num_seqs, max_context_len,
+                                                  window, dl.p.part, dl.plan);
+  return decode_kernel_launch(dl, s);
 }
 
 int pa_decode(void* out, void* workspace, size_t workspace_bytes, const void* q,
@@ -323,6 +378,80 @@ int pa_decode(void* out, void* workspace, size_t workspace_bytes, const void* q,
                      max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_heads,
                      num_kv_heads, head_dim, block_size, num_blocks, scale, softcap, window,
                      partition_size, dtype, stream, nullptr);
+}
+
+int pa_step(const pa_step_args* a, void* stream) {
+  if (!a) return PA_EINVAL;
+  const int T = a->num_tokens;
+  if (T < 0) return PA_EINVAL;
+  if (env_int("PA_STEP_FUSE", 1) == 0) {
+    // the three entry points one after another
+    int st = PA_OK;
+    if (T > 0) {
+      st = pa_reshape_and_cache(a->key, a->value, a->k_cache, a->v_cache, a->slot_mapping, T,
+                                a->num_blocks, a->block_size, a->num_kv_heads, a->head_dim,
+                                a->dtype, stream);
+      if (st != PA_OK) return st;
+    }
+    st = pa_decode(a->out, a->workspace, a->workspace_bytes, a->q, a->k_cache, a->v_cache,
+                   a->block_tables, a->max_blocks_per_seq, a->context_lens, a->max_context_len,
+                   a->num_seqs, a->num_heads, a->num_kv_heads, a->head_dim, a->block_size,
+                   a->num_blocks, a->scale, a->softcap, a->window, a->partition_size, a->dtype,
+                   stream);
+    if (st != PA_OK) return st;
+    return pa_decode_reduce(a->out, a->workspace, a->workspace_bytes, a->context_lens,
+                            a->max_context_len, a->num_seqs, a->num_heads, a->head_dim,
+                            a->partition_size, a->window, a->dtype, stream);
+  }
+  if (T > 0) {  // the checks of pa_reshape_and_cache
+    if (a->num_blocks <= 0 || a->num_kv_heads <= 0) return PA_EINVAL;
+    if (!valid_dtype(a->dtype) || !supported_head_dim(a->head_dim) ||
+        !pow2_in(a->block_size, 1, 256))
+      return PA_EUNSUPPORTED;
+    if (!a->key || !a->value || !a->k_cache || !a->v_cache || !a->slot_mapping) return PA_EINVAL;
+  }
+  DecodeLaunch dl;
+  bool empty = true;
+  int st = decode_setup(a->out, a->workspace, a->workspace_bytes, a->q, a->k_cache, a->v_cache,
+                        a->block_tables, a->max_blocks_per_seq, a->context_lens,
+                        a->max_context_len, a->num_seqs, a->num_heads, a->num_kv_heads,
+                        a->head_dim, a->block_size, a->num_blocks, a->scale, a->softcap,
+                        a->window, a->partition_size, a->dtype, nullptr, dl, &empty);
+  if (st != PA_OK) return st;
+  if (empty)
+    return T > 0 ? pa_reshape_and_cache(a->key, a->value, a->k_cache, a->v_cache,
+                                        a->slot_mapping, T, a->num_blocks, a->block_size,
+                                        a->num_kv_heads, a->head_dim, a->dtype, stream)
+                 : PA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // One launch before the decode kernel: the new K/V rows and the plan.
+  if (T > 0 || dl.need_plan) {
+    pa::PrepParams pp{};
+    pp.context_lens = a->context_lens;
+    pp.num_seqs = a->num_seqs;
+    pp.max_context_len = a->max_context_len;
+    pp.window = a->window;
+    pp.part = dl.p.part;
+    pp.plan = dl.plan;
+    if (!dl.need_plan) pp.plan.order = nullptr;
+    pp.key = static_cast<const uint4*>(a->key);
+    pp.value = static_cast<const uint4*>(a->value);
+    pp.k_cache = static_cast<uint4*>(a->k_cache);
+    pp.v_cache = static_cast<uint4*>(a->v_cache);
+    pp.slot_mapping = a->slot_mapping;
+    pp.num_tokens = T;
+    pp.num_slots = (int64_t)a->num_blocks * a->block_size;
+    pp.row16 = (int)((int64_t)a->num_kv_heads * a->head_dim * elem_bytes(a->dtype) / 16);
+    const long blocks = 1 + ((long)T + 3) / 4;
+    if (blocks > 0x7fffffffL) return PA_EUNSUPPORTED;
+    pa::step_prep_kernel<<<dim3((unsigned)blocks), dim3(1024), 0, s>>>(pp);
+    if (hipGetLastError() != hipSuccess) return PA_ELAUNCH;
+  }
+  st = decode_kernel_launch(dl, s);
+  if (st != PA_OK) return st;
+  return pa_decode_reduce(a->out, a->workspace, a->workspace_bytes, a->context_lens,
+                          a->max_context_len, a->num_seqs, a->num_heads, a->head_dim,
+                          a->partition_size, a->window, a->dtype, stream);
 }
 
 int pa_decode_reduce(void* out, const void* workspace, size_t workspace_bytes,

@@ -1,5 +1,4 @@
-// The layer step (reshape_and_cache + decode + reduce) as one call, and its
-// capture into a HIP graph for replay.
+// Capture of the layer step (pa_step) into a HIP graph for replay.
 #include <new>
 
 #include <hip/hip_runtime.h>
@@ -12,26 +11,6 @@ struct pa_step_graph {
 };
 
 extern "C" {
-
-int pa_step(const pa_step_args* a, void* stream) {
-  if (!a) return PA_EINVAL;
-  int st = PA_OK;
-  if (a->num_tokens > 0) {
-    st = pa_reshape_and_cache(a->key, a->value, a->k_cache, a->v_cache, a->slot_mapping,
-                              a->num_tokens, a->num_blocks, a->block_size, a->num_kv_heads,
-                              a->head_dim, a->dtype, stream);
-    if (st != PA_OK) return st;
-  }
-  st = pa_decode(a->out, a->workspace, a->workspace_bytes, a->q, a->k_cache, a->v_cache,
-                 a->block_tables, a->max_blocks_per_seq, a->context_lens, a->max_context_len,
-                 a->num_seqs, a->num_heads, a->num_kv_heads, a->head_dim, a->block_size,
-                 a->num_blocks, a->scale, a->softcap, a->window, a->partition_size, a->dtype,
-                 stream);
-  if (st != PA_OK) return st;
-  return pa_decode_reduce(a->out, a->workspace, a->workspace_bytes, a->context_lens,
-                          a->max_context_len, a->num_seqs, a->num_heads, a->head_dim,
-                          a->partition_size, a->window, a->dtype, stream);
-}
 
 int pa_step_graph_create(const pa_step_args* a, void* stream, pa_step_graph** out) {
   if (!a || !out || !stream) return PA_EINVAL;  // capture needs a created stream

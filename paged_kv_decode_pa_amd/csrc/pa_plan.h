@@ -59,10 +59,11 @@ __device__ __forceinline__ void expand_lists(const int* s_off, int nk, int total
   }
 }
 
-// part: partition size in tokens (max_context_len when keys are not split)
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ context_lens,
-                                                    int num_seqs, int max_context_len, int window,
-                                                    int part, Plan plan) {
+// The plan, built by one workgroup of 1024 threads.  part: partition size
+// in tokens (max_context_len when keys are not split).
+__device__ __forceinline__ void plan_body(const int32_t* __restrict__ context_lens, int num_seqs,
+                                          int max_context_len, int window, int part,
+                                          const Plan& plan) {
   constexpr int NBK = 256;
   __shared__ int hist[NBK];
   __shared__ int s_tmp[17];
@@ -124,6 +125,51 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     __syncthreads();
   }
   if (t == 0) *plan.num_items = base;
+}
+
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ context_lens,
+                                                    int num_seqs, int max_context_len, int window,
+                                                    int part, Plan plan) {
+  plan_body(context_lens, num_seqs, max_context_len, window, part, plan);
+}
+
+// What a layer step does before its decode launch, in one launch of
+// 1024-thread workgroups: workgroup 0 builds the plan (when plan.order is
+// set); workgroups 1.. copy the new K/V rows into their slots, four tokens
+// per workgroup (the copy of reshape_cache_kernel: 16-byte moves, slots
+// outside the cache skipped).
+struct PrepParams {
+  const int32_t* context_lens;
+  int num_seqs, max_context_len, window, part;
+  Plan plan;             // order null: no plan
+  const uint4* key;      // [num_tokens, row16]
+  const uint4* value;
+  uint4* k_cache;        // [num_slots, row16]
+  uint4* v_cache;
+  const int64_t* slot_mapping;
+  int num_tokens;
+  int64_t num_slots;
+  int row16;
+};
+
+__global__ __launch_bounds__(1024) void step_prep_kernel(PrepParams pp) {
+  if (blockIdx.x == 0) {
+    if (pp.plan.order != nullptr)
+      plan_body(pp.context_lens, pp.num_seqs, pp.max_context_len, pp.window, pp.part, pp.plan);
+    return;
+  }
+  const int i = (int)(blockIdx.x - 1) * 4 + (int)(threadIdx.x >> 8);
+  if (i >= pp.num_tokens) return;
+  const int64_t s = pp.slot_mapping[i];
+  if (s < 0 || s >= pp.num_slots) return;
+  const uint4* ks = pp.key + (int64_t)i * pp.row16;
+  const uint4* vs = pp.value + (int64_t)i * pp.row16;
+  uint4* kd = pp.k_cache + s * pp.row16;
+  uint4* vd = pp.v_cache + s * pp.row16;
+  for (int j = threadIdx.x & 255; j < pp.row16; j += 256) {
+    kd[j] = ks[j];
+    vd[j] = vs[j];
+  }
 }
 
 // Plan of a multi-query launch (one workgroup of 1024 threads):

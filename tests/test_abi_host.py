@@ -37,7 +37,8 @@ def test_status_strings():
 
 def test_workspace_size_arithmetic():
     # plan: order [B] int32, a 256-byte item count, items [B * NP] int32
-    # pairs (each padded to 256 B); then [B, Hq, NP, D] fp32 + two [B, Hq, NP] fp32
+    # pairs (each padded to 256 B); then, when split, [B, Hq, NP, D] fp32 +
+    # two [B, Hq, NP] fp32
     def pad(n):
         return (n + 255) // 256 * 256
 

@@ -1,7 +1,7 @@
-"""The layer step (reshape_and_cache + decode + reduce) through pa_step and
-through a captured HIP graph: every replay equals an eager run on the same
-inputs, with other eager work and synchronisations between replays, and
-replays follow input changes (nothing is cached)."""
+"""The layer step (reshape_and_cache + decode + merge) through pa_step and
+through a captured HIP graph: every replay equals an eager pa_step on the
+same inputs bit for bit, with other eager work and synchronisations between
+replays, and replays follow input changes (nothing is cached)."""
 import numpy as np
 import pytest
 
@@ -24,6 +24,12 @@ def test_step_graph_replays_match_eager(P):
     step = pa.Step(dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, c.scale,
                    c.softcap, c.window, partition_size=P, max_context_len=c.max_context_len,
                    key=dc.key, value=dc.value, slot_mapping=dc.slot_mapping)
+    # eager pa_step on the same buffers (its own output): the reference the
+    # replays must equal bit for bit
+    eager_step = pa.Step(dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens,
+                         c.scale, c.softcap, c.window, partition_size=P,
+                         max_context_len=c.max_context_len, key=dc.key, value=dc.value,
+                         slot_mapping=dc.slot_mapping)
     s = torch.cuda.Stream()
     step.capture(s)
     rng = np.random.default_rng(5)
@@ -36,12 +42,16 @@ def test_step_graph_replays_match_eager(P):
         with torch.cuda.stream(s):
             got = to_f64(step.replay(s).clone())
         s.synchronize()
-        eager = to_f64(pa.decode(dc.q, dc.k_cache, dc.v_cache, dc.block_tables,
-                                 dc.context_lens, c.scale, c.softcap, c.window,
-                                 partition_size=P, max_context_len=c.max_context_len))
+        eager = to_f64(eager_step.run().clone())
+        torch.cuda.synchronize()
         assert np.array_equal(got, eager), f"replay {r} differs from eager"
         want = oracle.decode_case(c)
         assert np.abs(got - want).max() <= 2e-2
+        # and so do the separate entry points
+        sep = to_f64(pa.decode(dc.q, dc.k_cache, dc.v_cache, dc.block_tables,
+                               dc.context_lens, c.scale, c.softcap, c.window,
+                               partition_size=P, max_context_len=c.max_context_len))
+        assert np.array_equal(got, sep), f"replay {r} differs from pa_decode + reduce"
         # unrelated eager work between replays
         x = torch.randn(1 << 20, device="cuda")
         (x * 2).sum().item()
