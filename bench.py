@@ -252,6 +252,8 @@ def bench_mq(args):
     cold_step_ms, cold_attn_ms = cold_times(step, min(args.steps, 20), dev)
     print(f"[bench] timed {args.steps} steps: {ms_step*1e3:.1f} us/step wall, "
           f"pa_mq_attention {attn_ms*1e3:.1f} us (HIP events)", file=sys.stderr, flush=True)
+    print(f"[bench] cold (caches evicted before each step): step {cold_step_ms*1e3:.1f} us, "
+          f"pa_mq_attention {cold_attn_ms*1e3:.1f} us", file=sys.stderr, flush=True)
     if args.calib_copy_mib:
         calibration_copy(args.calib_copy_mib, dev)
 

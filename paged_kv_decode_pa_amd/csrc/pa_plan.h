@@ -176,8 +176,10 @@ __global__ __launch_bounds__(1024) void step_prep_kernel(PrepParams pp) {
 //   vctx[tok] = context of query token tok (its position + 1, clamped to
 //   [0, max_context_len]); vrow[tok] = its sequence (per-token path);
 //   tiles = (sequence, first row) for every R rows of each sequence's
-//   n * G rows (tiled path), at most tile_cap of them, a sequence's last
-//   rows (the most keys) first.  Null outputs are skipped.
+//   n * G rows (tiled path), at most tile_cap of them: sequences with the
+//   most keys first (counting sort over 256 length buckets, when they are
+//   at most 4096), and within a sequence its last rows (the most keys)
+//   first, so the grid runs longest work first.  Null outputs are skipped.
 __global__ __launch_bounds__(1024) void mq_plan_kernel(const int32_t* __restrict__ query_start,
                                                        const int32_t* __restrict__ context_lens,
                                                        int num_seqs, int num_tokens,
@@ -185,11 +187,15 @@ __global__ __launch_bounds__(1024) void mq_plan_kernel(const int32_t* __restrict
                                                        int2* tiles, int tile_cap,
                                                        int32_t* num_tiles, int32_t* vctx,
                                                        int32_t* vrow) {
-  constexpr int kQS = 4096;  // sequence starts searched in LDS up to this many sequences
+  constexpr int kQS = 4096;  // sequences kept in LDS (starts, order) up to this many
+  constexpr int NBK = 256;
   __shared__ int s_tmp[17];
   __shared__ int s_off[1024];
   __shared__ int s_nt[1024];
+  __shared__ int s_seq[1024];
   __shared__ int s_qs[kQS + 1];
+  __shared__ int s_order[kQS];
+  __shared__ int hist[NBK];
   const int t = threadIdx.x;
   const bool in_lds = num_seqs + 1 <= kQS + 1;
   if (in_lds)
@@ -197,11 +203,32 @@ __global__ __launch_bounds__(1024) void mq_plan_kernel(const int32_t* __restrict
   __syncthreads();
   auto qstart = [&](int b) { return in_lds ? s_qs[b] : query_start[b]; };
   if (tiles != nullptr) {
+    if (in_lds) {
+      // sequences by attended length, longest first
+      const int span = max(max_context_len, 1);
+      auto bucket = [&](int b) {
+        const int L = min(max(context_lens[b], 0), max_context_len);
+        return NBK - 1 - (int)(((long long)L * (NBK - 1)) / span);
+      };
+      if (t < NBK) hist[t] = 0;
+      __syncthreads();
+      for (int b = t; b < num_seqs; b += blockDim.x) atomicAdd(&hist[bucket(b)], 1);
+      __syncthreads();
+      {
+        int total;
+        const int off = block_exclusive_scan(t < NBK ? hist[t] : 0, s_tmp, &total);
+        if (t < NBK) hist[t] = off;
+      }
+      __syncthreads();
+      for (int b = t; b < num_seqs; b += blockDim.x) s_order[atomicAdd(&hist[bucket(b)], 1)] = b;
+      __syncthreads();
+    }
     int base = 0;
     for (int k0 = 0; k0 < num_seqs; k0 += blockDim.x) {
-      const int b = k0 + t;
+      const int k = k0 + t;
+      const int b = k < num_seqs ? (in_lds ? s_order[k] : k) : 0;
       int nt = 0;
-      if (b < num_seqs) {
+      if (k < num_seqs) {
         // rows of the sequence's tokens that lie in [0, num_tokens)
         const int q0 = min(max(qstart(b), 0), num_tokens);
         const int n = min(max(qstart(b + 1) - q0, 0), num_tokens - q0);
@@ -210,10 +237,11 @@ __global__ __launch_bounds__(1024) void mq_plan_kernel(const int32_t* __restrict
       int total;
       s_off[t] = block_exclusive_scan(nt, s_tmp, &total);
       s_nt[t] = nt;
+      s_seq[t] = b;
       __syncthreads();
       const int room = max(tile_cap - base, 0);
       expand_lists(s_off, blockDim.x, min(total, room), [&](int kk, int i, int idx) {
-        tiles[base + idx] = make_int2(k0 + kk, (s_nt[kk] - 1 - i) * R);
+        tiles[base + idx] = make_int2(s_seq[kk], (s_nt[kk] - 1 - i) * R);
       });
       base += total;
       __syncthreads();
