@@ -70,6 +70,17 @@ def measured_traffic(digest: str, workload: str):
         return None
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(case, budget_s: float):
     """Time the oracle on the workload's sequences, in order, until `budget_s`
     seconds have been spent (whole passes over the batch are repeated when
@@ -106,7 +117,7 @@ def cpu_baseline(case, budget_s: float):
     cores = len(os.sched_getaffinity(0))
     return {"value": round(bytes_ / dt / 1e9, 4), "unit": "GB/s",
             "cores": blas_threads if blas_threads else cores,
-            "host_cores": cores, "kind": "oracle",
+            "host_cores": cores, "cpu_model": cpu_model(), "kind": "oracle",
             "seq_steps_per_s": round(seqs / dt, 2),
             "sample": f"float64 numpy oracle on this workload: reshape_and_cache of its {T} new "
                       f"rows then decode of its sequences in order, {seqs} sequence-steps over "
@@ -182,7 +193,7 @@ def cpu_baseline_mq(case, budget_s: float):
     dt = time.perf_counter() - t0
     cores = len(os.sched_getaffinity(0))
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle", "tokens_per_s": round(toks / dt, 2),
+            "cpu_model": cpu_model(), "kind": "oracle", "tokens_per_s": round(toks / dt, 2),
             "sample": f"float64 numpy oracle on this workload: reshape_and_cache of its "
                       f"{case.T} new rows, then {toks} of its {case.T} query tokens in order "
                       f"in {dt:.1f} s"}
@@ -248,7 +259,10 @@ def bench_mq(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    attn_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    attn_t = np.array([a.elapsed_time(b) for a, b in ev])
+    attn_ms = float(attn_t.mean())
+    attn_pct = {k: round(float(np.percentile(attn_t, q)) * 1e3, 2)
+                for k, q in (("p10", 10), ("p50", 50), ("p90", 90))}
     cold_step_ms, cold_attn_ms = cold_times(step, min(args.steps, 20), dev)
     print(f"[bench] timed {args.steps} steps: {ms_step*1e3:.1f} us/step wall, "
           f"pa_mq_attention {attn_ms*1e3:.1f} us (HIP events)", file=sys.stderr, flush=True)
@@ -319,6 +333,7 @@ def bench_mq(args):
         "tflops": round(flops / step_s / 1e12, 2),
         "us_per_layer_step": round(ms_step * 1e3, 2),
         "pa_mq_attention_us": round(attn_ms * 1e3, 2),
+        "pa_mq_attention_us_pct": attn_pct,
         "algorithmic_bytes_per_step": ab["total"],
         "max_abs_err_vs_oracle": max_err,
         "roofline": roof,
@@ -335,7 +350,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="4",
                     choices=["1", "2", "3", "4", "5", "spec5", "chunk512", "prefill"],
                     help="decode workload 1-5, or a multi-query workload")
@@ -344,6 +359,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--no-check", action="store_true", help="skip the parity spot-check")
+    ap.add_argument("--sweep-partitions", action="store_true",
+                    help="also time pa_step at partition sizes 0 (no split) and 64..1024")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay of the step")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -444,7 +461,10 @@ def main():
         ev.append(step(record=True))
     torch.cuda.synchronize()
     ms_step3 = (time.perf_counter() - t0) * 1e3 / args.steps
-    decode_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    dec_t = np.array([a.elapsed_time(b) for a, b in ev])
+    decode_ms = float(dec_t.mean())
+    decode_pct = {k: round(float(np.percentile(dec_t, q)) * 1e3, 2)
+                  for k, q in (("p10", 10), ("p50", 50), ("p90", 90))}
     print(f"[bench] three calls: {ms_step3*1e3:.1f} us/step wall, "
           f"pa_decode {decode_ms*1e3:.1f} us (HIP events)", file=sys.stderr, flush=True)
 
@@ -454,6 +474,34 @@ def main():
     print(f"[bench] cold (caches evicted before each step): pa_step {cold_step_ms*1e3:.1f} us, "
           f"three calls {cold_step3_ms*1e3:.1f} us, pa_decode {cold_decode_ms*1e3:.1f} us",
           file=sys.stderr, flush=True)
+
+    sweep = None
+    if args.sweep_partitions:
+        sweep = []
+        for ps in [0, 64, 128, 256, 512, 1024]:
+            if ps % case.bs:
+                continue
+            st_s = pa.Step(q, kc, vc, bt, cl, case.scale, case.softcap, case.window,
+                           partition_size=ps, max_context_len=maxL, key=key, value=value,
+                           slot_mapping=slots)
+            for _ in range(args.warmup):
+                st_s.run()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                st_s.run()
+            torch.cuda.synchronize()
+            w_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+            def sweep_step(record=False, st_s=st_s):
+                st_s.run()
+                return None
+            c_ms, _ = cold_times(sweep_step, reps, dev)
+            sweep.append({"partition_size": ps, "step_us": round(w_ms * 1e3, 2),
+                          "cold_step_us": round(c_ms * 1e3, 2)})
+            print(f"[bench] sweep P={ps}: pa_step {w_ms*1e3:.1f} us warm, {c_ms*1e3:.1f} us cold",
+                  file=sys.stderr, flush=True)
+            del st_s
 
     # the same step captured once into a HIP graph and replayed K times
     graph = None
@@ -537,6 +585,7 @@ def main():
         "us_per_layer_step": round(ms_step * 1e3, 2),
         "algorithmic_bytes_per_step": ab["total"],
         "pa_decode_us": round(decode_ms * 1e3, 2),
+        "pa_decode_us_pct": decode_pct,
         "split_k_reduce": bool(split),
         "max_abs_err_vs_oracle": max_err,
         "roofline": {
@@ -554,6 +603,7 @@ def main():
                         "value": round(ab["total"] / (ms_step3 / 1e3) / 1e9, 2), "unit": "GB/s",
                         "note": "reshape_and_cache, pa_decode, pa_decode_reduce as separate calls"},
         "graph_replay": graph,
+        "partition_sweep": sweep,
         "cold": {"step_us": round(cold_step_ms * 1e3, 2),
                  "three_calls_step_us": round(cold_step3_ms * 1e3, 2),
                  "pa_decode_us": round(cold_decode_ms * 1e3, 2),

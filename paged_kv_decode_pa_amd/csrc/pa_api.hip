@@ -131,8 +131,11 @@ int pa_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads, int 
   const int span = window > 0 ? (window < max_context_len ? window : max_context_len)
                               : max_context_len;
   const long units = (long)num_seqs * num_kv_heads;
-  // plenty of (sequence, head) units and short contexts: no split
-  if (units >= 4L * kNumCUs && span <= 2048) return 0;
+  // enough (sequence, head) units for the contexts' length: no split, so no
+  // partials and no reduce launch (measured through pa_step: 64 sequences of
+  // up to 1024 tokens x 4 heads, 37.6 us unsplit vs 39.4 us at 512-token
+  // partitions, caches cold)
+  if ((units >= kNumCUs && span <= 1024) || (units >= 4L * kNumCUs && span <= 2048)) return 0;
   int part = 512;
   if (part % block_size) part = block_size;
   return part;

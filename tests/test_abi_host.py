@@ -60,6 +60,16 @@ def test_partition_choice_is_a_multiple_of_block_size():
             assert P >= 0 and P % bs == 0
 
 
+def test_partition_choice_splits_only_long_or_few():
+    # enough (sequence, KV head) units for short contexts: one partition
+    assert pa.partition_size(64, 8, 4, 256, 16, 1024) == 0
+    assert pa.partition_size(512, 8, 4, 256, 16, 2048) == 0
+    # long contexts or few units: 512-token partitions
+    assert pa.partition_size(16, 8, 4, 256, 16, 8192) == 512
+    assert pa.partition_size(8, 8, 4, 256, 16, 1024) == 512
+    assert pa.partition_size(33, 32, 4, 64, 32, 131072) == 512
+
+
 def decode_args(**over):
     a = dict(out=FAKE, ws=None, ws_bytes=0, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, maxb=8,
              cl=FAKE, maxL=128, B=2, Hq=8, Hkv=2, D=64, bs=16, NB=64, scale=0.125,
