@@ -263,11 +263,16 @@ def bench_mq(args):
     attn_ms = float(attn_t.mean())
     attn_pct = {k: round(float(np.percentile(attn_t, q)) * 1e3, 2)
                 for k, q in (("p10", 10), ("p50", 50), ("p90", 90))}
-    cold_step_ms, cold_attn_ms = cold_times(step, min(args.steps, 20), dev)
     print(f"[bench] timed {args.steps} steps: {ms_step*1e3:.1f} us/step wall, "
           f"pa_mq_attention {attn_ms*1e3:.1f} us (HIP events)", file=sys.stderr, flush=True)
-    print(f"[bench] cold (caches evicted before each step): step {cold_step_ms*1e3:.1f} us, "
-          f"pa_mq_attention {cold_attn_ms*1e3:.1f} us", file=sys.stderr, flush=True)
+    cold = None
+    if not args.no_cold:
+        cold_step_ms, cold_attn_ms = cold_times(step, min(args.steps, 20), dev)
+        print(f"[bench] cold (caches evicted before each step): step {cold_step_ms*1e3:.1f} us, "
+              f"pa_mq_attention {cold_attn_ms*1e3:.1f} us", file=sys.stderr, flush=True)
+        cold = {"step_us": round(cold_step_ms * 1e3, 2),
+                "pa_mq_attention_us": round(cold_attn_ms * 1e3, 2),
+                "note": "median over steps each preceded by reading a 1 GiB scratch buffer"}
     if args.calib_copy_mib:
         calibration_copy(args.calib_copy_mib, dev)
 
@@ -337,9 +342,7 @@ def bench_mq(args):
         "algorithmic_bytes_per_step": ab["total"],
         "max_abs_err_vs_oracle": max_err,
         "roofline": roof,
-        "cold": {"step_us": round(cold_step_ms * 1e3, 2),
-                 "pa_mq_attention_us": round(cold_attn_ms * 1e3, 2),
-                 "note": "median over steps each preceded by reading a 1 GiB scratch buffer"},
+        "cold": cold,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
@@ -359,6 +362,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--no-check", action="store_true", help="skip the parity spot-check")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cache-evicted timing (profiling runs: warm launches only)")
     ap.add_argument("--sweep-partitions", action="store_true",
                     help="also time pa_step at partition sizes 0 (no split) and 64..1024")
     ap.add_argument("--no-graph", action="store_true",
@@ -469,11 +474,18 @@ def main():
           f"pa_decode {decode_ms*1e3:.1f} us (HIP events)", file=sys.stderr, flush=True)
 
     reps = min(args.steps, 20)
-    cold_step_ms, _ = cold_times(fused_step, reps, dev)
-    cold_step3_ms, cold_decode_ms = cold_times(step, reps, dev)
-    print(f"[bench] cold (caches evicted before each step): pa_step {cold_step_ms*1e3:.1f} us, "
-          f"three calls {cold_step3_ms*1e3:.1f} us, pa_decode {cold_decode_ms*1e3:.1f} us",
-          file=sys.stderr, flush=True)
+    cold = None
+    if not args.no_cold:
+        cold_step_ms, _ = cold_times(fused_step, reps, dev)
+        cold_step3_ms, cold_decode_ms = cold_times(step, reps, dev)
+        print(f"[bench] cold (caches evicted before each step): pa_step {cold_step_ms*1e3:.1f} us, "
+              f"three calls {cold_step3_ms*1e3:.1f} us, pa_decode {cold_decode_ms*1e3:.1f} us",
+              file=sys.stderr, flush=True)
+        cold = {"step_us": round(cold_step_ms * 1e3, 2),
+                "three_calls_step_us": round(cold_step3_ms * 1e3, 2),
+                "pa_decode_us": round(cold_decode_ms * 1e3, 2),
+                "pa_decode_gbs": round(case.algorithmic_bytes()["decode"] / (cold_decode_ms / 1e3) / 1e9, 2),
+                "note": "median over steps each preceded by reading a 1 GiB scratch buffer"}
 
     sweep = None
     if args.sweep_partitions:
@@ -604,11 +616,7 @@ def main():
                         "note": "reshape_and_cache, pa_decode, pa_decode_reduce as separate calls"},
         "graph_replay": graph,
         "partition_sweep": sweep,
-        "cold": {"step_us": round(cold_step_ms * 1e3, 2),
-                 "three_calls_step_us": round(cold_step3_ms * 1e3, 2),
-                 "pa_decode_us": round(cold_decode_ms * 1e3, 2),
-                 "pa_decode_gbs": round(ab["decode"] / (cold_decode_ms / 1e3) / 1e9, 2),
-                 "note": "median over steps each preceded by reading a 1 GiB scratch buffer"},
+        "cold": cold,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
