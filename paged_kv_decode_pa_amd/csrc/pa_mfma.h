@@ -93,8 +93,8 @@ struct MfmaShape {
 };
 
 // byte offset of (row r, element d) of a V chunk in LDS: 16-byte segments
-// XOR-swizzled by (r / 4) mod 4, so the four lane groups of a transposed
-// gather hit distinct LDS banks
+// XOR-swizzled by (r / 4) mod 4 (measured: a swizzle that also separates the
+// four rows of one transposing read's lane group changes nothing)
 template <int D>
 __device__ __forceinline__ int v_swz(int r) { return ((r >> 2) & 3) << 1; }
 
@@ -105,20 +105,27 @@ __device__ __forceinline__ uint32_t v_lds_off(int r, int d) {
 
 // A operand of P.V for head-dim tile mt: lane (c16, j) gets V[16t + 4j +
 // i][16mt + c16], i < 4, for each 16-token tile t, as 4 packed 16-bit values
-// per tile, gathered from the chunk in LDS.
+// per tile, from the chunk in LDS by one transposing read per tile
+// (ds_read_b64_tr_b16).  That read hands lane i of each 16-lane group
+// element i % 4 of the 8 bytes at the address of lane 4e + i / 4, as its
+// element e; so lane (c16, j) supplies the address of V row 16t + 4j +
+// c16 / 4, dims 16mt + 4 (c16 % 4) .. + 3 (8 contiguous bytes: the swizzle
+// moves whole 16-byte segments), and receives its column of the 4 x 16
+// block of rows 16t + 4j .. + 3.
 template <int D, int TILES>
 __device__ __forceinline__ void vt_frag(const char* vb, int mt, int c16, int j,
                                         uint32_t (&vv)[2 * TILES]) {
-  const int d = 16 * mt + c16;
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  const int d = 16 * mt + 4 * (c16 & 3);
 #pragma unroll
-  for (int t = 0; t < TILES; ++t)
-#pragma unroll
-    for (int i2 = 0; i2 < 2; ++i2) {
-      const int r0 = 16 * t + 4 * j + 2 * i2;
-      const uint16_t lo16 = *reinterpret_cast<const uint16_t*>(vb + v_lds_off<D>(r0, d));
-      const uint16_t hi16 = *reinterpret_cast<const uint16_t*>(vb + v_lds_off<D>(r0 + 1, d));
-      vv[2 * t + i2] = (uint32_t)lo16 | ((uint32_t)hi16 << 16);
-    }
+  for (int t = 0; t < TILES; ++t) {
+    const int r = 16 * t + 4 * j + (c16 >> 2);
+    const i16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(vb + v_lds_off<D>(r, d)));
+    const uint2 u = __builtin_bit_cast(uint2, x);
+    vv[2 * t] = u.x;
+    vv[2 * t + 1] = u.y;
+  }
 }
 
 // true when any lane's alpha is below 1 (its running max moved): only then

@@ -247,3 +247,21 @@ def test_mq_many_sequences():
         got = DeviceMQ(c).run(tiled=tiled, shared=shared)
         toks, want = _sampled(c, 200, 5)
         check(got, want, "bf16", rows=toks)
+
+
+@pytest.mark.parametrize("P,W", [(0, 0), (64, 0), (64, 100), (512, 0)])
+def test_mq_mixed_batch(P, W):
+    """Prompt chunks beside decoding sequences, empty sequences and drafts of
+    a few tokens in one call, on the shared kernel and on the per-token
+    path: every token matches the oracle."""
+    from gpu_util import say
+    say(f"mq mixed batch P={P} W={W}")
+    rng = np.random.default_rng(300 + P + W)
+    L = [700, 1, 300, 64, 0, 1200, 33, 500, 90, 257]
+    n = [96, 1, 1, 64, 0, 1, 5, 1, 40, 1]
+    c = make_mq_case(Hq=8, Hkv=4, D=256, bs=16, dtype="bf16", context_lens=L, query_lens=n,
+                     softcap=50.0, window=W, partition_size=P, seed=int(rng.integers(1 << 30)),
+                     new_rows=True)
+    want = oracle.multi_query_case(c)
+    check(DeviceMQ(c).run(shared=True), want, "bf16")
+    check(DeviceMQ(c).run(tiled=False), want, "bf16")
