@@ -603,6 +603,9 @@ def main():
         "roofline": {
             "bound": "hbm",
             "kernel": "pa_decode",
+            "timed": ("HIP events around each pa_decode call on its stream: the plan kernel "
+                      "(when the launch uses one) and the decode kernel; the rocprofv3 summary "
+                      "lists the two separately"),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
