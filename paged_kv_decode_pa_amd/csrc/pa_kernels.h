@@ -522,17 +522,21 @@ __global__ __launch_bounds__(64 * kMaxWaves, PA_DECODE_MIN_WAVES) void decode_ke
 }
 
 // One workgroup of four wavefronts per (sequence, query head): merge the
-// partials of sequences that span more than one non-empty partition.  A
-// partial row (D floats) is read as float4 by D/4 lanes, so a wavefront
-// takes 64/(D/4) partitions per step and the four wavefronts interleave;
-// the per-lane sums meet through xor shuffles and LDS.
+// partials of sequences that span more than one non-empty partition, in one
+// pass over them.  A partial row (D floats) is read as float4 by D/4 lanes,
+// so a wavefront takes 64/(D/4) partitions per step and the four wavefronts
+// interleave.  Each lane keeps a running maximum M, weight sum and weighted
+// row, rescaled by 2^(M_old - M_new) when a partition raises M (the online
+// softmax again, over partitions), so the loads of a partition's maximum,
+// sum and row are issued together; lanes then combine through xor shuffles
+// and LDS with one more rescale.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
   constexpr int LPP = D / 4;     // lanes per partition row
   constexpr int PPW = 64 / LPP;  // partition rows per wavefront step
   constexpr int NWV = 4;
   typedef const __attribute__((address_space(4))) float cfloat;
-  __shared__ float s_red[NWV];
+  __shared__ float s_m[NWV];
   __shared__ float s_o[NWV][D];
   __shared__ float s_den[NWV];
   const int t = threadIdx.x;
@@ -551,42 +555,62 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
   cfloat* ml = (cfloat*)(p.max_logits + base);
   cfloat* es = (cfloat*)(p.exp_sums + base);
 
-  // the largest partition maximum
-  float M = kNegInf;
-  for (int q = p0 + t; q <= p1; q += 256) M = fmaxf(M, p.max_logits[base + q]);
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, shfl_xor_f(M, m));
-  if (lane == 0) s_red[w] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-
   const int sub = lane / LPP;  // which of the step's partitions
   const int dl = lane % LPP;   // float4 of the row
+  float M = kNegInf, den = 0.0f;
   f32x4_t o = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float den = 0.0f;
   const float* src = p.tmp_out + base * D + 4 * dl;
 #pragma unroll 4
   for (int q = p0 + w * PPW + sub; q <= p1; q += NWV * PPW) {
-    const float wq = es[q] * fast_exp2(ml[q] - M);
-    den += dl == 0 ? wq : 0.0f;
-    o += wq * *reinterpret_cast<const f32x4_t*>(src + (size_t)q * D);
+    const float mq = ml[q];
+    const float lq = es[q];
+    const f32x4_t row = *reinterpret_cast<const f32x4_t*>(src + (size_t)q * D);
+    const float Mn = fmaxf(M, mq);
+    const float a = fast_exp2(M - Mn);   // 0 while M is still -inf
+    const float wq = lq * fast_exp2(mq - Mn);
+    den = den * a + wq;
+    o = o * a + wq * row;
+    M = Mn;
   }
+  // lanes of one float4 column across the step's partitions, then waves
 #pragma unroll
   for (int m = LPP; m < 64; m <<= 1) {
-    o[0] += shfl_xor_f(o[0], m);
-    o[1] += shfl_xor_f(o[1], m);
-    o[2] += shfl_xor_f(o[2], m);
-    o[3] += shfl_xor_f(o[3], m);
+    const float Mo = shfl_xor_f(M, m);
+    const float Mn = fmaxf(M, Mo);
+    // a lane that saw no partition keeps M = -inf and zero sums
+    const float a = Mn == kNegInf ? 0.0f : fast_exp2(M - Mn);
+    const float ao = Mn == kNegInf ? 0.0f : fast_exp2(Mo - Mn);
+    den = den * a + shfl_xor_f(den, m) * ao;
+    f32x4_t oo;
+    oo[0] = shfl_xor_f(o[0], m);
+    oo[1] = shfl_xor_f(o[1], m);
+    oo[2] = shfl_xor_f(o[2], m);
+    oo[3] = shfl_xor_f(o[3], m);
+    o = o * a + oo * ao;
+    M = Mn;
   }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) den += shfl_xor_f(den, m);
-  if (sub == 0) *reinterpret_cast<f32x4_t*>(&s_o[w][4 * dl]) = o;
-  if (lane == 0) s_den[w] = den;
+  if (sub == 0) {
+    *reinterpret_cast<f32x4_t*>(&s_o[w][4 * dl]) = o;
+    if (dl == 0) {
+      s_m[w] = M;
+      s_den[w] = den;
+    }
+  }
   __syncthreads();
-  const float inv = 1.0f / (s_den[0] + s_den[1] + s_den[2] + s_den[3]);
+  const float Mg = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+  float f[NWV];
+  float tot = 0.0f;
+#pragma unroll
+  for (int v = 0; v < NWV; ++v) {
+    f[v] = s_m[v] == kNegInf ? 0.0f : fast_exp2(s_m[v] - Mg);
+    tot += s_den[v] * f[v];
+  }
+  const float inv = 1.0f / tot;
   for (int d = t; d < D; d += 256) {
-    const float v = (s_o[0][d] + s_o[1][d] + s_o[2][d] + s_o[3][d]) * inv;
-    store_elem<DT>(p.out, ((size_t)b * p.num_heads + hq) * D + d, v);
+    float v = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NWV; ++k) v += s_o[k][d] * f[k];
+    store_elem<DT>(p.out, ((size_t)b * p.num_heads + hq) * D + d, v * inv);
   }
 }
 
