@@ -283,3 +283,69 @@ def test_many_sequences(P):
                   partition_size=P, poison=False)
     sample = sorted(set(rng.choice(B, size=60, replace=False).tolist()) | {int(np.argmax(L))})
     check(c, gpu(c), seqs=sample)
+
+
+# --------------------------------------------------------------------------
+# maximum sizes: KV pools past 4 GiB (64-bit page offsets) and the largest
+# block size
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dt,Hq,Hkv,D,bs,cap,P", [
+    ("bf16", 8, 4, 256, 16, 50.0, 256),   # vector kernel
+    ("f16", 32, 4, 64, 32, 0.0, 512),     # matrix-core kernel
+])
+def test_pool_beyond_4gib(dt, Hq, Hkv, D, bs, cap, P):
+    """A small case whose pages sit at the top of K and V pools of more than
+    4 GiB each (built on the GPU, NaN everywhere else): page offsets past
+    2^32 bytes, for decode and for a new row written by reshape_and_cache."""
+    import torch
+    import paged_kv_decode_pa_amd as pa
+    from gpu_util import TORCH_DT, say, to_f64, upload
+    say(f"pool beyond 4 GiB {dt} G={Hq // Hkv} D={D} bs={bs}")
+    L = [1, 40, 333, 1000]
+    c = make_case(B=4, Hq=Hq, Hkv=Hkv, D=D, bs=bs, dtype=dt, context_lens=L, softcap=cap,
+                  partition_size=P, seed=41, new_rows=True)
+    page = bs * Hkv * D * 2
+    NB_big = (9 << 29) // page + 7           # 4.5 GiB per cache, plus a few pages
+    assert NB_big * page > (1 << 32)
+    dev = torch.device("cuda")
+    tdt = TORCH_DT[dt]
+    kc = torch.full((NB_big, bs, Hkv, D), float("nan"), dtype=tdt, device=dev)
+    vc = torch.full((NB_big, bs, Hkv, D), float("nan"), dtype=tdt, device=dev)
+    # the case's pool block i -> block NB_big - 1 - i (the top of the pool)
+    remap = NB_big - 1 - np.arange(c.NB)
+    ids = torch.from_numpy(remap).to(dev)
+    kc[ids] = upload(c.k_cache, dt)
+    vc[ids] = upload(c.v_cache, dt)
+    bt = torch.from_numpy(np.where(c.block_tables >= 0,
+                                   remap[np.maximum(c.block_tables, 0)], -1).astype(np.int32)).to(dev)
+    slots = np.where(c.slot_mapping >= 0,
+                     remap[c.slot_mapping // bs] * bs + c.slot_mapping % bs, -1).astype(np.int64)
+    assert slots.max() * Hkv * D * 2 > (1 << 32)
+    pa.reshape_and_cache(upload(c.key, dt), upload(c.value, dt), kc, vc,
+                         torch.from_numpy(slots).to(dev))
+    out = pa.decode(upload(c.q, dt), kc, vc, bt, torch.from_numpy(c.context_lens).to(dev),
+                    c.scale, c.softcap, c.window, partition_size=P,
+                    max_context_len=c.max_context_len)
+    torch.cuda.synchronize()
+    check(c, to_f64(out))
+    # copy-on-write between two blocks above 4 GiB: bit-exact
+    src, dst = int(remap[0]), int(NB_big - 1 - c.NB - 3)
+    pa.copy_blocks(kc, vc, torch.tensor([[src, dst]], dtype=torch.int64, device=dev))
+    torch.cuda.synchronize()
+    assert torch.equal(kc[dst].view(torch.int16), kc[src].view(torch.int16))
+    assert torch.equal(vc[dst].view(torch.int16), vc[src].view(torch.int16))
+    del kc, vc
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dt,Hq,Hkv,D,P", [("bf16", 8, 2, 128, 0), ("f32", 4, 4, 64, 512),
+                                           ("f16", 16, 2, 64, 256)])
+def test_block_size_256(dt, Hq, Hkv, D, P):
+    """The largest supported block size: chunks inside one page, contexts of
+    one page, a ragged page tail and several pages."""
+    from gpu_util import say
+    say(f"block size 256 {dt} G={Hq // Hkv} D={D} P={P}")
+    L = [1, 255, 256, 257, 700, 1300]
+    c = make_case(B=len(L), Hq=Hq, Hkv=Hkv, D=D, bs=256, dtype=dt, context_lens=L,
+                  softcap=30.0, partition_size=P, seed=43, new_rows=True, extra_table_cols=1)
+    check(c, gpu(c))
