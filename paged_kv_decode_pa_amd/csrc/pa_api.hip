@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <atomic>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/pa.h"
@@ -43,6 +45,20 @@ int env_int(const char* name, int dflt) {
   const char* v = getenv(name);
   if (!v || !*v) return dflt;
   return atoi(v);
+}
+
+// Workgroups one CU holds at once for a launch shape, from the runtime's
+// occupancy calculator (query(&n) fills n), remembered in *slot; <= 0 when
+// unknown.
+template <typename Query>
+int blocks_per_cu(std::atomic<int>* slot, Query&& query) {
+  int v = slot->load(std::memory_order_relaxed);
+  if (v == 0) {
+    int n = 0;
+    v = query(&n) && n > 0 ? n : -1;
+    slot->store(v, std::memory_order_relaxed);
+  }
+  return v;
 }
 
 // Wavefronts per workgroup: enough to split a partition's chunks while each
@@ -693,6 +709,22 @@ int pa_mq_attention(void* out, void* workspace, size_t workspace_bytes, const vo
     const long blocks = max_tiles * num_kv_heads * np;
     if (blocks > 0x7fffffffL) return PA_EUNSUPPORTED;
     const dim3 grid((unsigned)blocks);
+    // per-wavefront kernel, keys not split: when the chip holds the whole
+    // grid, tiles go to positions so that each CU's tiles pair long with
+    // short (resident_tile; the shared kernel measured no better with it);
+    // PA_MQ_RESIDENT=0 keeps the plan order
+    const bool resident = np == 1 && env_int("PA_MQ_RESIDENT", 1) != 0;
+    // wavefront priority by remaining chunks, in steps of 4 (measured on
+    // the speculative-verification batch against steps of 1-12 and none);
+    // PA_MQ_PRIO sets the step, 0 switches it off
+    p.prio = env_int("PA_MQ_PRIO", 4);
+    const int dti = dtype == PA_F16 ? 0 : 1;
+    const int di = head_dim == 64 ? 0 : head_dim == 128 ? 1 : 2;
+    auto set_resident = [&](int wgs_per_tile, int occ) {
+      if (occ <= 0 || kNumCUs % wgs_per_tile) return;
+      p.resident_period = kNumCUs / wgs_per_tile;
+      p.resident_span = occ * p.resident_period;
+    };
     bool ok;
     if (wg) {
       const int tiles_per_chunk = block_size >= 32 && head_dim <= 128 ? 2 : 1;
@@ -715,6 +747,21 @@ int pa_mq_attention(void* out, void* workspace, size_t workspace_bytes, const vo
                                  (int)(blocks < (1L << 30) ? blocks : (1L << 30)));
       while (!heads && nw > 1 && nw * lds_wave > PA_WG_LDS_CAP) nw /= 2;
       const dim3 g_grid((unsigned)(heads ? blocks / num_kv_heads : blocks));
+      if (resident) {
+        static std::atomic<int> occ_mq[2 * 3 * 5 * 3 * 2 * 9];
+        set_resident(heads ? 1 : num_kv_heads,
+                     blocks_per_cu(
+                         &occ_mq[((((dti * 3 + di) * 5 + nr) * 3 + tiles_per_chunk) * 2 + heads) *
+                                     9 +
+                                 nw],
+                         [&](int* n) {
+                           return dtype == PA_F16
+                                      ? pa::launch_mq_mfma_f16(head_dim, nr, tiles_per_chunk,
+                                                               heads, nw, g_grid, s, p, n)
+                                      : pa::launch_mq_mfma_bf16(head_dim, nr, tiles_per_chunk,
+                                                                heads, nw, g_grid, s, p, n);
+                         }));
+      }
       ok = dtype == PA_F16
                ? pa::launch_mq_mfma_f16(head_dim, nr, tiles_per_chunk, heads, nw, g_grid, s, p)
                : pa::launch_mq_mfma_bf16(head_dim, nr, tiles_per_chunk, heads, nw, g_grid, s, p);

@@ -25,11 +25,13 @@ size_t decode_mfma_lds_bytes(int D, int G, int tiles);
 
 // Tiled multi-query path (f16/bf16, block_size >= 16 * tiles); nr 16-row
 // blocks per wavefront.  Returns false when not built for the shape.
-// heads: one wavefront per KV head (nw = num_kv_heads).
+// heads: one wavefront per KV head (nw = num_kv_heads).  With blocks_per_cu
+// set, nothing is launched: it receives how many such workgroups one CU
+// holds at once.
 bool launch_mq_mfma_f16(int D, int nr, int tiles, bool heads, int nw, dim3 grid, hipStream_t s,
-                        const MQParams& p);
+                        const MQParams& p, int* blocks_per_cu = nullptr);
 bool launch_mq_mfma_bf16(int D, int nr, int tiles, bool heads, int nw, dim3 grid, hipStream_t s,
-                         const MQParams& p);
+                         const MQParams& p, int* blocks_per_cu = nullptr);
 size_t mq_mfma_lds_bytes(int D, int nr, int tiles, bool heads);
 
 // Workgroup-shared multi-query path (four wavefronts of 16 * nr rows each).
@@ -96,9 +98,17 @@ bool launch_mq_wg_bf16(int D, int nr, int tiles, int nbuf, dim3 grid, hipStream_
   case (DV * 8 + NRV) * 4 + TV: {                                                   \
     if (heads) {                                                                    \
       const size_t lds = (size_t)nw * sizeof(float) * MQShape<DT, DV, NRV, TV, true>::LDS_FLOATS; \
+      if (blocks_per_cu)                                                            \
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(                        \
+                   blocks_per_cu, mq_mfma_kernel<DT, DV, NRV, TV, true>, 64 * nw, lds) == \
+               hipSuccess;                                                          \
       mq_mfma_kernel<DT, DV, NRV, TV, true><<<grid, dim3(64 * nw), lds, s>>>(p);     \
     } else {                                                                        \
       const size_t lds = (size_t)nw * sizeof(float) * MQShape<DT, DV, NRV, TV>::LDS_FLOATS; \
+      if (blocks_per_cu)                                                            \
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(                        \
+                   blocks_per_cu, mq_mfma_kernel<DT, DV, NRV, TV, false>, 64 * nw, lds) == \
+               hipSuccess;                                                          \
       mq_mfma_kernel<DT, DV, NRV, TV><<<grid, dim3(64 * nw), lds, s>>>(p);           \
     }                                                                               \
     return true;                                                                    \
@@ -109,7 +119,7 @@ bool launch_mq_wg_bf16(int D, int nr, int tiles, int nbuf, dim3 grid, hipStream_
 // fragments stay in registers)
 #define PA_DEFINE_MQ_LAUNCHER(NAME, DT)                                             \
   bool NAME(int D, int nr, int tiles, bool heads, int nw, dim3 grid, hipStream_t s,  \
-            const MQParams& p) {                                                    \
+            const MQParams& p, int* blocks_per_cu) {                                \
     switch ((D * 8 + nr) * 4 + tiles) {                                             \
       PA_MQ_CASE(DT, 64, 1, 1) PA_MQ_CASE(DT, 64, 1, 2)                             \
       PA_MQ_CASE(DT, 64, 2, 1) PA_MQ_CASE(DT, 64, 2, 2)                             \

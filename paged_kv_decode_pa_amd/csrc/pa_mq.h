@@ -54,9 +54,29 @@ struct MQParams {
   int num_parts;
   int max_tiles;              // grid tiles per (KV head, partition)
   int num_tokens;             // T
+  int resident_period;        // tiles per round of one workgroup per CU (0: plan order)
+  int resident_span;          // tiles the chip holds at once
+  int prio;                   // chunks per wave-priority step (0: none)
   float qk_mul;
   float cap_mul;
 };
+
+// Position -> plan tile when the whole grid is resident from the start.
+// Workgroups i and i + period then share a CU for the whole launch (the
+// dispatcher fills every CU once per round, in the same CU order each
+// round), so plain longest-first order would put the longest tiles of every
+// round on the same CUs.  Odd rounds take their tiles in reverse (a partial
+// last round reverses what it has), so each CU pairs a long tile with a
+// short one.  A grid larger than the chip keeps the plan order: its later
+// workgroups go wherever a slot frees, longest first.
+__device__ __forceinline__ int resident_tile(int i, int n, int period, int span) {
+  if (period <= 0 || n > span) return i;
+  const int r = i / period;
+  if ((r & 1) == 0) return i;
+  const int base = r * period;
+  const int m = min(period, n - base);
+  return base + (m - 1) - (i - base);
+}
 
 template <int DT, int D, int NR, int TILES, bool HEADS = false>
 struct MQShape {
@@ -109,9 +129,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
   const int rest = HEADS ? (int)blockIdx.x : (int)(blockIdx.x / p.num_kv_heads);
   const int cw = HEADS ? 0 : w;       // first chunk of this wavefront
   const int cstride = HEADS ? 1 : nw;  // its chunk stride
-  const int tile = rest % p.max_tiles;
   const int part = rest / p.max_tiles;
-  if (tile >= *(cint32*)p.num_tiles) return;
+  const int n_tiles = *(cint32*)p.num_tiles;
+  if (rest % p.max_tiles >= n_tiles) return;
+  const int tile = resident_tile(rest % p.max_tiles, n_tiles, p.resident_period, p.resident_span);
   const uint64_t tl = ((cu64*)p.tiles)[tile];
   const int b = (int)(uint32_t)tl;
   const int f0 = (int)(uint32_t)(tl >> 32);
@@ -372,6 +393,17 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma clang loop unroll(disable)
     for (; c <= c1; c += 2 * cstride) {
+      // issue priority from the chunks this wavefront has left, in steps of
+      // p.prio chunks: the wavefronts sharing a SIMD are otherwise served
+      // oldest first, so a CU's older workgroup would finish long before
+      // the younger one, which then runs alone
+      if (p.prio) {
+        const int rem = (c1 - c) / cstride;
+        if (rem >= 4 * p.prio) __builtin_amdgcn_s_setprio(3);
+        else if (rem >= 2 * p.prio) __builtin_amdgcn_s_setprio(2);
+        else if (rem >= p.prio) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
       step(c, c + 2 * cstride, kf0, vb0);
       step(c + cstride, c + 3 * cstride, kf1, vb1);
     }

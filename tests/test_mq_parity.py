@@ -265,3 +265,27 @@ def test_mq_mixed_batch(P, W):
     want = oracle.multi_query_case(c)
     check(DeviceMQ(c).run(shared=True), want, "bf16")
     check(DeviceMQ(c).run(tiled=False), want, "bf16")
+
+
+@pytest.mark.parametrize("B", [400, 700])
+@pytest.mark.parametrize("path", ["wave", "wave-split"])
+def test_mq_resident_order(B, path):
+    """Per-wavefront kernel, grids of several resident rounds (one tile per
+    sequence, about 0.8 B tiles; a round is 256 workgroups):
+    the position -> tile map that reverses odd rounds (a partial one
+    included) covers every tile once.  Output matches the oracle, and
+    equals the plan-order launch (PA_MQ_RESIDENT=0) bit for bit."""
+    from gpu_util import say, to_f64
+    say(f"mq resident order B={B} path={path}")
+    rng = np.random.default_rng(900 + B)
+    n = rng.integers(0, 5, size=B)
+    L = n + rng.integers(0, 120, size=B)
+    c = make_mq_case(Hq=4, Hkv=2, D=64, bs=16, dtype="bf16", context_lens=L, query_lens=n,
+                     softcap=30.0, partition_size=0, seed=int(rng.integers(1 << 30)),
+                     new_rows=True)
+    tiled, shared, env = PATHS[path]
+    dev = DeviceMQ(c)
+    got = dev.run(tiled=tiled, shared=shared, env=env)
+    check(got, oracle.multi_query_case(c), "bf16")
+    ref = dev.run(tiled=tiled, shared=shared, env={**(env or {}), "PA_MQ_RESIDENT": "0"})
+    assert np.array_equal(to_f64(got), to_f64(ref))
