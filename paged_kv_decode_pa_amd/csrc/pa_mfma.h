@@ -280,7 +280,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
   // refilled with chunk cn (a few bytes of q past the last chunk), so DEPTH
   // chunks stay in flight while this one is computed.  A chunk past the end
   // is fully masked and leaves the running state unchanged.
-  auto step = [&](int cc, int cn, uint4 (&k)[TILES][KS], char* vb) {
+  auto step = [&](int cc, int cn, uint4 (&k)[TILES][KS], char* vb) __attribute__((always_inline)) {
     f32x4_t sc[TILES];
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
@@ -386,11 +386,23 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
       vcopy(a, vbuf + i * S::VBYTES);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (DEPTH == 2) {
+      // the two V buffers as restrict pointers: the compiler's own wait
+      // before one buffer's LDS reads then leaves the other buffer's copy in
+      // flight (the explicit wait in step covers what the reads need)
+      auto two = [&](char* __restrict__ b0, char* __restrict__ b1) __attribute__((always_inline)) {
+        step(c, c + 2 * cstride, kf[0], b0);
+        step(c + cstride, c + 3 * cstride, kf[1], b1);
+      };
 #pragma clang loop unroll(disable)
-    for (; c <= c1; c += DEPTH * cstride) {
+      for (; c <= c1; c += 2 * cstride) two(vbuf, vbuf + S::VBYTES);
+    } else {
+#pragma clang loop unroll(disable)
+      for (; c <= c1; c += DEPTH * cstride) {
 #pragma unroll
-      for (int i = 0; i < DEPTH; ++i)
-        step(c + i * cstride, c + (i + DEPTH) * cstride, kf[i], vbuf + i * S::VBYTES);
+        for (int i = 0; i < DEPTH; ++i)
+          step(c + i * cstride, c + (i + DEPTH) * cstride, kf[i], vbuf + i * S::VBYTES);
+      }
     }
   }
   // drain the trailing loads before the wavefront moves on

@@ -277,7 +277,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
   };
 
   // One chunk cc, then its K slot and V buffer are refilled with chunk cn.
-  auto step = [&](int cc, int cn, uint4 (&k)[TILES][KS], char* vb) {
+  auto step = [&](int cc, int cn, uint4 (&k)[TILES][KS], char* vb) __attribute__((always_inline)) {
     f32x4_t sc[NR][TILES];
 #pragma unroll
     for (int nb = 0; nb < NR; ++nb)
@@ -391,6 +391,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
     __builtin_amdgcn_sched_barrier(0);
     vcopy(a, vb1);
     __builtin_amdgcn_sched_barrier(0);
+    // the two V buffers as restrict pointers: the compiler's own wait before
+    // one buffer's LDS reads then leaves the other buffer's copy in flight
+    // (the explicit wait in step covers what the reads need)
+    auto two = [&](char* __restrict__ b0, char* __restrict__ b1) __attribute__((always_inline)) {
+      step(c, c + 2 * cstride, kf0, b0);
+      step(c + cstride, c + 3 * cstride, kf1, b1);
+    };
 #pragma clang loop unroll(disable)
     for (; c <= c1; c += 2 * cstride) {
       // issue priority from the chunks this wavefront has left, in steps of
@@ -404,8 +411,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
         else if (rem >= p.prio) __builtin_amdgcn_s_setprio(1);
         else __builtin_amdgcn_s_setprio(0);
       }
-      step(c, c + 2 * cstride, kf0, vb0);
-      step(c + cstride, c + 3 * cstride, kf1, vb1);
+      two(vb0, vb1);
     }
   }
   // drain the trailing loads (the V buffers are reused below)
@@ -636,7 +642,7 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
     ld_row[k] = r;
     ld_seg[k] = head_bytes + (uint32_t)((sg ^ (q < LOADS ? k_swz<D>(r) : v_swz<D>(r))) * 16);
   }
-  auto issue = [&](int c, int buf) {
+  auto issue = [&](int c, char* kb) {
     rsrc_t kr, vr;
     uint32_t soff = 0;
     int rlo = 0, rhi = 0;
@@ -647,6 +653,10 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
         pg0 = cpg;
         const int pg = cpg + lane;
         tbl_v = pg <= last_pg ? bt[pg] : 0;
+        // (every 64 pages) wait here: a load still pending where the paths
+        // join would make the compiler wait for every copy in flight on
+        // each chunk
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
       }
       int phys = __builtin_amdgcn_readlane(tbl_v, cpg - pg0);
       phys = ((unsigned)phys < (unsigned)p.num_blocks) ? phys : 0;
@@ -660,7 +670,6 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
       kr = make_rsrc(dummy, (uint32_t)(G * D * EB));
       vr = kr;
     }
-    char* kb = lds + buf * 2 * CBYTES;
 #pragma unroll
     for (int k = 0; k < LPW; ++k) {
       const int q = LPW * w + k;
@@ -684,21 +693,24 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
   const int c0 = lo / NT;
   const int c1 = (hi - 1) / NT;
 #pragma unroll
-  for (int k = 0; k < NBUF - 1; ++k) issue(c0 + k, k);
-  int buf = 0;
-#pragma clang loop unroll(disable)
-  for (int c = c0; c <= c1; ++c) {
-    // this wavefront's copies of chunk c are done; the barrier makes every
-    // wavefront's copies visible, and every wavefront is past chunk c - 1,
-    // so its buffer can take chunk c + NBUF - 1
+  for (int k = 0; k < NBUF - 1; ++k) issue(c0 + k, lds + k * 2 * CBYTES);
+  // Chunk c from buffer kb; next (chunk c - 1's buffer) takes chunk
+  // c + NBUF - 1.  This wavefront's copies of chunk c are done at the wait;
+  // the barrier makes every wavefront's copies visible and puts every
+  // wavefront past chunk c - 1.  That wait and barrier are all the ordering
+  // the copies need: the barrier carries no release fence (which would wait
+  // for every copy in flight), and kb and next are restrict, so the
+  // compiler's own wait before the LDS reads does not cover the copy just
+  // issued into the other buffer.
+  auto chunk = [&](int c, const char* __restrict__ kb, char* __restrict__ next)
+                   __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(vmcnt_only((NBUF - 2) * LPW));
-    __syncthreads();
-    issue(c + NBUF - 1, buf == 0 ? NBUF - 1 : buf - 1);
-    const char* kb = lds + buf * 2 * CBYTES;
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    issue(c + NBUF - 1, next);
     const char* vb = kb + CBYTES;
-    buf = buf == NBUF - 1 ? 0 : buf + 1;
     const int cs = c * NT;
-    if (wlo >= whi || cs + NT <= wlo || cs >= whi) continue;  // no row of this wavefront looks here
+    if (wlo >= whi || cs + NT <= wlo || cs >= whi) return;  // no row of this wavefront looks here
 
     f32x4_t sc[NR][TILES];
 #pragma unroll
@@ -785,6 +797,13 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
                                      acc[nb][mt]);
       }
     }
+  };
+  int buf = 0;
+#pragma clang loop unroll(disable)
+  for (int c = c0; c <= c1; ++c) {
+    const int nxt = buf == 0 ? NBUF - 1 : buf - 1;
+    chunk(c, lds + buf * 2 * CBYTES, lds + nxt * 2 * CBYTES);
+    buf = buf == NBUF - 1 ? 0 : buf + 1;
   }
   // the copies issued past the last chunk must land before the workgroup
   // (and its LDS) goes away
