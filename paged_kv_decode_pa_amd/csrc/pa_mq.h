@@ -538,6 +538,14 @@ struct MQWGShape {
   static_assert(CBYTES % 1024 == 0 && (2 * LOADS) % NW == 0, "chunk shape");
 };
 
+// How far (base-2 logit units) a row's logits may pass its reference
+// maximum before the shared kernel moves it and rescales the accumulators.
+// The reference is exact for the result (sum, accumulators and a partial's
+// max all use it); only the probabilities grow, below 2^kMaxSlack, which the
+// 16-bit P operand and fp32 sums hold without loss of relative precision.
+// Most chunks then skip the rescale.
+constexpr float kMaxSlack = 8.0f;
+
 // K rows in LDS: 16-byte segment s of row r is stored at s ^ k_swz(r)
 template <int D>
 __device__ __forceinline__ int k_swz(int r) {
@@ -731,8 +739,13 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
     uint32_t pk[NR][2 * TILES];
 #pragma unroll
     for (int nb = 0; nb < NR; ++nb) {
+      // logits in base-2 units are pr * smul: soft-capped ones come out of
+      // the cap already scaled, plain ones keep the scale for the exponent's
+      // fma below
       float pr[TILES][4];
-      if (p.cap_mul > 0.0f) {
+      const bool capped = p.cap_mul > 0.0f;
+      const float smul = capped ? 1.0f : p.qk_mul;
+      if (capped) {
 #pragma unroll
         for (int t = 0; t < TILES; ++t)
 #pragma unroll
@@ -741,7 +754,7 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
 #pragma unroll
         for (int t = 0; t < TILES; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pr[t][i] = sc[nb][t][i] * p.qk_mul;
+          for (int i = 0; i < 4; ++i) pr[t][i] = sc[nb][t][i];
       }
       float cmax = kNegInf;
       if (cs < full_lo || cs + NT > full_hi) {  // keys some row of the wavefront must not see
@@ -759,19 +772,28 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
         for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, pr[t][i]);
       cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
       cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
-      const float m_new = fmaxf(m_run[nb], cmax);
-      const float m_use = m_new == kNegInf ? 0.0f : m_new;
-      const float alpha = fast_exp2(m_run[nb] - m_use);
+      // The row's reference maximum moves only when a logit passes it by
+      // more than kMaxSlack (and on the row's first key: -inf + slack is
+      // -inf), so most chunks skip the rescale; probabilities stay below
+      // 2^kMaxSlack, and sum, accumulators and the partial's max all use the
+      // same reference.  A row with no key yet keeps (-inf, 0, 0) and uses 0
+      // as the exponent base.
+      const float m_cand = fmaxf(m_run[nb], cmax * smul);
+      float alpha = 1.0f;
+      if (m_cand > m_run[nb] + kMaxSlack) {
+        alpha = fast_exp2(m_run[nb] - m_cand);
+        m_run[nb] = m_cand;
+      }
+      const float m_use = m_run[nb] == kNegInf ? 0.0f : m_run[nb];
       float psum = 0.0f;
 #pragma unroll
       for (int t = 0; t < TILES; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pr[t][i] = fast_exp2(pr[t][i] - m_use);
+          pr[t][i] = fast_exp2(__builtin_fmaf(pr[t][i], smul, -m_use));
           psum += pr[t][i];
         }
       l_run[nb] = l_run[nb] * alpha + psum;
-      m_run[nb] = m_new;
       if (any_rescale(alpha)) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[nb][mt] *= alpha;

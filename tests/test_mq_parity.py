@@ -289,3 +289,19 @@ def test_mq_resident_order(B, path):
     check(got, oracle.multi_query_case(c), "bf16")
     ref = dev.run(tiled=tiled, shared=shared, env={**(env or {}), "PA_MQ_RESIDENT": "0"})
     assert np.array_equal(to_f64(got), to_f64(ref))
+
+
+@pytest.mark.parametrize("cap", [0.0, 30.0])
+def test_mq_shared_kernel_wide_logits(cap):
+    """Logits 16x the usual spread (scale 2 at head_dim 64): a row's running
+    maximum then jumps by more than the kernel's slack within a prompt, so
+    both the rescale and the keep-the-reference branches of the shared
+    kernel's online softmax run, with and without soft-capping."""
+    from gpu_util import say
+    say(f"mq shared kernel wide logits cap={cap}")
+    c = make_mq_case(Hq=16, Hkv=2, D=64, bs=32, dtype="f16", context_lens=[300, 170],
+                     query_lens=[300, 90], scale=2.0, softcap=cap, partition_size=128,
+                     seed=4242 + int(cap), new_rows=True)
+    want = oracle.multi_query_case(c)
+    check(DeviceMQ(c).run(shared=True), want, "f16")
+    check(DeviceMQ(c).run(shared=True, partition_size=0), oracle.multi_query_case(c), "f16")
