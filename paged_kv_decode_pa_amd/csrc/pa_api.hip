@@ -291,6 +291,35 @@ static int decode_setup(void* out, void* workspace, size_t workspace_bytes, cons
   while (!heads && nw > 1 && nw * lds_wave > PA_WG_LDS_CAP) nw /= 2;
   const long blocks = (long)num_seqs * (heads ? 1 : num_kv_heads) * np;
   if (blocks > 0x7fffffffL) return PA_EUNSUPPORTED;
+  // Vector kernel: when the whole grid fits the chip at once as two-wavefront
+  // workgroups, at least two per CU, take those, with wave priority from the
+  // chunks each wavefront has left, so the workgroups sharing a CU finish
+  // together rather than oldest first (sliding-window workload 53.1 ->
+  // 49.7 us, against eight-wavefront workgroups).  PA_DECODE_PRIO sets the
+  // priority step (0: off); a forced PA_DECODE_WAVES keeps its count.
+  bool resident_pairs = false;
+  if (!mfma && nw > 2 && env_int("PA_DECODE_WAVES", 0) == 0 && blocks >= 2L * kNumCUs) {
+    static std::atomic<int> occ_dec[3 * 3 * 4 * 2];
+    const int paged_k = block_size >= nt;
+    const int di = head_dim == 64 ? 0 : head_dim == 128 ? 1 : 2;
+    const int gi = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
+    const int occ = blocks_per_cu(&occ_dec[((dtype * 3 + di) * 4 + gi) * 2 + paged_k], [&](int* n) {
+      const dim3 blk(128);
+      switch (dtype) {
+        case PA_F32: return pa::launch_decode_f32(head_dim, G, paged_k, false, dim3(1), blk, nullptr, p, n);
+        case PA_F16: return pa::launch_decode_f16(head_dim, G, paged_k, false, dim3(1), blk, nullptr, p, n);
+        default: return pa::launch_decode_bf16(head_dim, G, paged_k, false, dim3(1), blk, nullptr, p, n);
+      }
+    });
+    // (the grid of a split launch is rounded up to whole XCD rounds)
+    const long grid2 = np > 1 ? (blocks + 8L * num_kv_heads - 1) / (8L * num_kv_heads) * 8L * num_kv_heads
+                              : blocks;
+    if (occ > 0 && grid2 <= (long)occ * kNumCUs) {
+      nw = 2;
+      resident_pairs = true;
+    }
+  }
+  p.prio = mfma ? 0 : env_int("PA_DECODE_PRIO", resident_pairs ? 2 : 0);
   // One workgroup per (sequence, KV head, partition), unless that grid is
   // more than twice what the chip holds at once and spans many partitions:
   // workgroups are dispatched at a bounded rate, so a grid of mostly empty

@@ -56,6 +56,7 @@ struct DecodeParams {
   float qk_mul;            // multiplies q.k
   float cap_mul;           // > 0: logit2 = cap_mul * tanh(q.k * qk_mul)
   int xcd_units;           // > 0: XCD-grouped grid over this many (b, p) units
+  int prio;                // chunks per wave-priority step (0: none)
 };
 
 struct ReduceParams {
@@ -403,6 +404,16 @@ __global__ __launch_bounds__(64 * kMaxWaves, PA_DECODE_MIN_WAVES) void decode_ke
 
 #pragma clang loop unroll(disable)
   for (; c <= c1; c += nw) {
+    // issue priority from the chunks this wavefront has left, in steps of
+    // p.prio chunks (workgroups sharing a CU then finish together rather
+    // than oldest first)
+    if (p.prio) {
+      const int rem = (c1 - c) / nw;
+      if (rem >= 4 * p.prio) __builtin_amdgcn_s_setprio(3);
+      else if (rem >= 2 * p.prio) __builtin_amdgcn_s_setprio(2);
+      else if (rem >= p.prio) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     // q.k partial sums over this lane's slice of each row
     float dots[NV];
 #pragma unroll

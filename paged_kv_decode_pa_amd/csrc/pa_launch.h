@@ -9,10 +9,15 @@
 
 namespace pa {
 
-// Each returns false when (head_dim, group) has no instantiation.
-bool launch_decode_f32(int D, int G, bool paged, bool loop, dim3 grid, dim3 block, hipStream_t s, const DecodeParams& p);
-bool launch_decode_f16(int D, int G, bool paged, bool loop, dim3 grid, dim3 block, hipStream_t s, const DecodeParams& p);
-bool launch_decode_bf16(int D, int G, bool paged, bool loop, dim3 grid, dim3 block, hipStream_t s, const DecodeParams& p);
+// Each returns false when (head_dim, group) has no instantiation.  With
+// blocks_per_cu set, nothing is launched: it receives how many such
+// workgroups one CU holds at once.
+bool launch_decode_f32(int D, int G, bool paged, bool loop, dim3 grid, dim3 block, hipStream_t s,
+                       const DecodeParams& p, int* blocks_per_cu = nullptr);
+bool launch_decode_f16(int D, int G, bool paged, bool loop, dim3 grid, dim3 block, hipStream_t s,
+                       const DecodeParams& p, int* blocks_per_cu = nullptr);
+bool launch_decode_bf16(int D, int G, bool paged, bool loop, dim3 grid, dim3 block, hipStream_t s,
+                        const DecodeParams& p, int* blocks_per_cu = nullptr);
 
 // Matrix-core path (f16/bf16, G in {8, 16}, block_size >= 16); returns
 // false when not built for the shape.
@@ -48,6 +53,14 @@ bool launch_mq_wg_bf16(int D, int nr, int tiles, int nbuf, dim3 grid, hipStream_
   {                                                                                 \
     const size_t lds = (block.x / 64) * sizeof(float) *                             \
                        DecodeShape<DT, DV, GV>::LDS_FLOATS;                          \
+    if (blocks_per_cu)                                                              \
+      return hipOccupancyMaxActiveBlocksPerMultiprocessor(                          \
+                 blocks_per_cu,                                                     \
+                 paged ? (loop ? decode_kernel<DT, DV, GV, true, true>              \
+                               : decode_kernel<DT, DV, GV, true, false>)            \
+                       : (loop ? decode_kernel<DT, DV, GV, false, true>             \
+                               : decode_kernel<DT, DV, GV, false, false>),          \
+                 block.x, lds) == hipSuccess;                                       \
     if (paged && loop) decode_kernel<DT, DV, GV, true, true><<<grid, block, lds, s>>>(p);   \
     else if (paged) decode_kernel<DT, DV, GV, true, false><<<grid, block, lds, s>>>(p);     \
     else if (loop) decode_kernel<DT, DV, GV, false, true><<<grid, block, lds, s>>>(p);      \
@@ -57,7 +70,7 @@ bool launch_mq_wg_bf16(int D, int nr, int tiles, int nbuf, dim3 grid, hipStream_
 
 #define PA_DEFINE_DECODE_LAUNCHER(NAME, DT)                                         \
   bool NAME(int D, int G, bool paged, bool loop, dim3 grid, dim3 block, hipStream_t s, \
-            const DecodeParams& p) {                                                \
+            const DecodeParams& p, int* blocks_per_cu) {                            \
     switch (D * 16 + G) {                                                           \
       PA_DECODE_CASE(DT, 64, 1) PA_DECODE_CASE(DT, 64, 2)                           \
       PA_DECODE_CASE(DT, 64, 4) PA_DECODE_CASE(DT, 64, 8)                           \

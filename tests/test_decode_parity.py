@@ -49,10 +49,23 @@ def test_workload2_gemma_global_with_new_rows(P):
 
 
 def test_workload3_gemma_sliding_window():
+    """The default launch here is the whole grid resident as two-wavefront
+    workgroups with wave priority; eight-wavefront workgroups (no priority)
+    must agree with the oracle too, and priority on or off changes only the
+    schedule: identical bits."""
+    import os
     from gpu_util import say
     say("workload 3")
     c = workload(3)
-    check(c, gpu(c))
+    got = gpu(c)
+    check(c, got)
+    check(c, gpu(c, waves=8))
+    os.environ["PA_DECODE_PRIO"] = "0"
+    try:
+        same = gpu(c)
+    finally:
+        os.environ.pop("PA_DECODE_PRIO", None)
+    assert np.array_equal(got, same)
 
 
 @pytest.mark.parametrize("P", [None, 0, 256])
