@@ -292,13 +292,17 @@ static int decode_setup(void* out, void* workspace, size_t workspace_bytes, cons
   const long blocks = (long)num_seqs * (heads ? 1 : num_kv_heads) * np;
   if (blocks > 0x7fffffffL) return PA_EUNSUPPORTED;
   // Vector kernel: when the whole grid fits the chip at once as two-wavefront
-  // workgroups, at least two per CU, take those, with wave priority from the
-  // chunks each wavefront has left, so the workgroups sharing a CU finish
-  // together rather than oldest first (sliding-window workload 53.1 ->
-  // 49.7 us, against eight-wavefront workgroups).  PA_DECODE_PRIO sets the
-  // priority step (0: off); a forced PA_DECODE_WAVES keeps its count.
+  // workgroups, at least four per CU, over partitions of 32+ chunks, take
+  // those, with wave priority from the chunks each wavefront has left, so
+  // the workgroups sharing a CU finish together rather than oldest first
+  // (sliding-window workload 53.1 -> 49.7 us, against eight-wavefront
+  // workgroups; 128- to 512-token splits of the 64-sequence global layer,
+  // with fewer workgroups or shorter partitions, lost 2-3 us to it).
+  // PA_DECODE_PRIO sets the priority step (0: off); a forced
+  // PA_DECODE_WAVES keeps its count.
   bool resident_pairs = false;
-  if (!mfma && nw > 2 && env_int("PA_DECODE_WAVES", 0) == 0 && blocks >= 2L * kNumCUs) {
+  if (!mfma && nw > 2 && env_int("PA_DECODE_WAVES", 0) == 0 && blocks >= 4L * kNumCUs &&
+      span >= 32 * nt) {
     static std::atomic<int> occ_dec[3 * 3 * 4 * 2];
     const int paged_k = block_size >= nt;
     const int di = head_dim == 64 ? 0 : head_dim == 128 ? 1 : 2;
