@@ -59,15 +59,20 @@ def to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
 # --------------------------------------------------------------------------
 def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping):
     """Return copies of the caches with row i of key/value written at slot
-    slot_mapping[i] (slot = physical_block * block_size + offset); a slot of
-    -1 is skipped.  Pure bit copies: the result is exact."""
+    slot_mapping[i] (slot = physical_block * block_size + offset).  Only the
+    new token's row is written (ovshake/nano-vllm README, "Key Concepts
+    Explained: KV Cache").  A slot that names no slot of the pool -- -1, the
+    usual "no slot" mark, or any value outside [0, num_blocks * block_size)
+    -- is skipped (reading: the pages define no such slot; the library's
+    contract for it is to leave the caches untouched).  Pure bit copies: the
+    result is exact."""
     kc = k_cache.copy()
     vc = v_cache.copy()
     NB, bs, Hkv, D = kc.shape
     kf = kc.reshape(NB * bs, Hkv, D)
     vf = vc.reshape(NB * bs, Hkv, D)
     for i, s in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
-        if s < 0:
+        if s < 0 or s >= NB * bs:
             continue
         kf[s] = key[i]
         vf[s] = value[i]

@@ -382,6 +382,29 @@ def test_reshape_and_cache_scatter(dtype):
     assert nv.tobytes() == want_v.tobytes()
 
 
+def test_reshape_and_cache_skips_slots_outside_the_pool():
+    """Slots that name no slot of the pool (-1, other negatives, and every
+    value >= num_blocks * block_size) leave both caches bit for bit as they
+    were; the in-pool rows of the same call still land.  Checked against a
+    slot-by-slot write of only the in-pool rows."""
+    rng = np.random.default_rng(31)
+    NB, bs, Hkv, D = 5, 4, 2, 8
+    kc = encode(rng.standard_normal((NB, bs, Hkv, D)).astype(np.float32), "bf16")
+    vc = encode(rng.standard_normal((NB, bs, Hkv, D)).astype(np.float32), "bf16")
+    slots = np.array([NB * bs, 3, -1, NB * bs + 7, -5, 19, 2 ** 40], dtype=np.int64)
+    key = encode(rng.standard_normal((len(slots), Hkv, D)).astype(np.float32), "bf16")
+    val = encode(rng.standard_normal((len(slots), Hkv, D)).astype(np.float32), "bf16")
+    nk, nv = O.reshape_and_cache(key, val, kc, vc, slots)
+    want_k, want_v = kc.copy(), vc.copy()
+    want_k[0, 3], want_v[0, 3] = key[1], val[1]      # slot 3
+    want_k[4, 3], want_v[4, 3] = key[5], val[5]      # slot 19, the pool's last
+    assert nk.tobytes() == want_k.tobytes()
+    assert nv.tobytes() == want_v.tobytes()
+    # only out-of-pool slots: nothing changes
+    nk, nv = O.reshape_and_cache(key[:1], val[:1], kc, vc, slots[:1])
+    assert nk.tobytes() == kc.tobytes() and nv.tobytes() == vc.tobytes()
+
+
 # --------------------------------------------------------------------------
 # planted mistakes: every mutant of the oracle must fail some pin above
 # --------------------------------------------------------------------------
