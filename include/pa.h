@@ -69,9 +69,18 @@ const char* pa_status_string(int status);
 /*
  * Write the K/V rows of new tokens into their physical slots:
  *   k_cache.flat[slot_mapping[i]] = key[i], v_cache.flat[...] = value[i]
- * with flat = view [num_blocks*block_size, num_kv_heads, head_dim].  Rows
- * with slot -1 are skipped; slots outside the pool are skipped as well.  The
- * copy is bit-exact (NaN payloads included).  Other slots are not touched.
+ * with flat = view [num_blocks*block_size, num_kv_heads, head_dim].  With a
+ * KV cache, a step computes K and V for its new tokens only and appends them
+ * to what is cached (ovshake/nano-vllm README, "Key Concepts Explained: KV
+ * Cache"); the cache is the block pool of the same section's PagedAttention
+ * figure, so a token's slot is physical_block * block_size + offset.  Rows
+ * with slot -1 are skipped; slots outside the pool (negative, or >=
+ * num_blocks * block_size) are skipped as well, leaving the caches untouched.
+ * The copy is bit-exact (NaN payloads included).  Other slots are not
+ * touched.  key, value and slot_mapping are read only; k_cache and v_cache
+ * are written in place.  Errors: PA_EINVAL for a negative num_tokens, a
+ * non-positive pool size or head count, or a null pointer when num_tokens >
+ * 0; PA_EUNSUPPORTED for the shapes below; PA_ELAUNCH if the launch fails.
  * Supported: dtype any; head_dim in {64,128,256}; block_size a power of two
  * in [1,256]; num_tokens >= 0 (0 is a no-op).
  */
@@ -101,14 +110,25 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, i
 
 /*
  * The partition size the library would pick for this shape (tokens per
- * split-K partition; 0 means one partition per sequence).  Host-only.
+ * split-K partition; 0 means one partition per sequence).  A partition is
+ * one block of the blocked, numerically stable attention the pages describe
+ * for flash attention (sourcepulse MinivLLM summary, "How It Works"): each
+ * is attended on its own and the blocks are merged by pa_decode_reduce.
+ * Host-only; returns 0 for non-positive sizes.
  */
 int pa_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads,
                              int head_dim, int block_size, int max_context_len,
                              int window, pa_dtype dtype);
 
 /*
- * Bytes of workspace pa_decode needs (0 only when num_seqs <= 0):
+ * Bytes of workspace pa_decode needs (0 only when num_seqs <= 0).  It holds
+ * the work order and, when keys are split into partitions (the blocks of
+ * blocked attention: sourcepulse MinivLLM summary, "How It Works"), each
+ * block's partial result -- its running maximum, its sum of exponentials and
+ * its normalised output -- for pa_decode_reduce to merge.  The caller
+ * allocates it in device memory and passes it to pa_decode and
+ * pa_decode_reduce; its contents need no initialisation.  Host-only;
+ * returns 0 for invalid sizes.  Layout:
  *   order      [num_seqs] int32, padded to 256 bytes: the sequences sorted
  *              longest first, written by pa_decode itself
  *   count      one int32, padded to 256 bytes, and
@@ -154,9 +174,18 @@ int pa_decode(void* out, void* workspace, size_t workspace_bytes,
 /*
  * Decode attention, reduce pass: for each sequence with more than one
  * non-empty partition, combine the partials with weights
- * exp_sum_p * 2^(max_logit_p - max_p' max_logit_p') and write `out`.
+ * exp_sum_p * 2^(max_logit_p - max_p' max_logit_p') and write `out`.  This
+ * is the merge step of blocked, numerically stable attention (sourcepulse
+ * MinivLLM summary, "How It Works": attention computed block by block): each
+ * block's result is rescaled to the common maximum before the sums are
+ * combined, so the output equals softmax attention over all the keys.
  * Sequences handled by pa_decode alone are left as they are.  A no-op when
- * partition_size is 0.  Arguments must match the pa_decode call.
+ * partition_size is 0.  Arguments must match the pa_decode call;
+ * `workspace` is the one pa_decode wrote (read only here) and
+ * `workspace_bytes` its size, checked against pa_decode_workspace_size
+ * (PA_EWORKSPACE when null or smaller).  `out` is written for merged sequences only.
+ * Errors: PA_EINVAL for negative sizes or null pointers, PA_EUNSUPPORTED
+ * for an unsupported dtype or head_dim, PA_ELAUNCH if the launch fails.
  */
 int pa_decode_reduce(void* out, const void* workspace, size_t workspace_bytes,
                      const int32_t* context_lens, int max_context_len,

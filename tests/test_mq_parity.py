@@ -68,9 +68,11 @@ class DeviceMQ:
 def check(got_t, want, dtype, rows=None):
     from gpu_util import to_f64
     got = to_f64(got_t)
+    # every output row, compared or not, must be finite: a read of a
+    # NaN-poisoned slot anywhere shows up here
+    assert np.isfinite(got).all(), "non-finite output"
     if rows is not None:
         got = got[rows]
-    assert np.isfinite(got).all(), "non-finite output"
     err = np.abs(got - want).max() if got.size else 0.0
     assert err <= TOL[dtype], f"max abs error {err:.3g} > {TOL[dtype]}"
     return err
@@ -222,12 +224,31 @@ def _sampled(c, k, seed):
     return toks, np.stack(want)
 
 
-@pytest.mark.parametrize("name", ["spec5", "chunk512", "prefill"])
-def test_mq_workloads_sampled(name):
+@pytest.mark.parametrize("name", ["spec5", "chunk512"])
+def test_mq_workloads_every_token(name):
+    """The speculative-verification (2,560 tokens) and chunked-prefill (575
+    tokens) workloads at full size, launched as the bench launches them:
+    every token against the oracle."""
     from gpu_util import say
     say(f"mq workload {name}")
     c = mq_workload(name)
     got = DeviceMQ(c).run()
+    check(got, oracle.multi_query_case(c), c.dtype)
+
+
+def test_mq_workload_prefill():
+    """Whole-prompt prefill, 4 x 2,048 tokens: every token of the first
+    prompt against the oracle, 48 sampled tokens of the others, and every
+    output row finite."""
+    from gpu_util import say
+    say("mq workload prefill")
+    c = mq_workload("prefill")
+    got = DeviceMQ(c).run()
+    kc, vc = O.reshape_and_cache(c.key, c.value, c.k_cache, c.v_cache, c.slot_mapping)
+    n0 = int(c.query_start[1])
+    want0 = O.multi_query(c.q[:n0], c.query_start[:2], kc, vc, c.block_tables[:1],
+                          c.context_lens[:1], c.scale, c.softcap, c.window, c.dtype)
+    check(got, want0, c.dtype, rows=np.arange(n0))
     toks, want = _sampled(c, 48, 7)
     check(got, want, c.dtype, rows=toks)
 
