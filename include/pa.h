@@ -60,7 +60,9 @@ typedef enum {
   PA_EINVAL = -1,        /* bad pointer, size or value                      */
   PA_EUNSUPPORTED = -2,  /* valid but not built: dtype, head_dim, group size */
   PA_EWORKSPACE = -3,    /* workspace missing or smaller than required      */
-  PA_ELAUNCH = -4        /* the HIP runtime refused the launch              */
+  PA_ELAUNCH = -4,       /* the HIP runtime refused the launch              */
+  PA_ESCRATCH = -5       /* pa_step_static: the step needs more scratch than
+                            PA_STATIC_SCRATCH_BYTES                         */
 } pa_status;
 
 /* Text for a status code (static storage, never NULL). */
@@ -301,6 +303,29 @@ int pa_step_graph_launch(pa_step_graph* graph, void* stream);
 
 /* Frees the graph (NULL is a no-op). */
 int pa_step_graph_destroy(pa_step_graph* graph);
+
+/* Size of the scratch array pa_step_static uses, per GPU (128 MiB). */
+#define PA_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/*
+ * pa_step without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc.  The step's scratch (sequence order, work list,
+ * split-K partials) lives in a file-scope device array of
+ * PA_STATIC_SCRATCH_BYTES bytes, one per GPU, held from the first call on
+ * that GPU until the process ends; args->workspace and
+ * args->workspace_bytes are ignored.  The array's device address is looked
+ * up once per device, on the first call with that device current (`stream`
+ * must belong to the current device).  Returns PA_ESCRATCH, before anything
+ * is enqueued, when pa_decode_workspace_size for the arguments exceeds
+ * PA_STATIC_SCRATCH_BYTES; otherwise the status and results of pa_step, bit
+ * for bit.  Nothing here allocates or frees.  Every call on one GPU shares
+ * that GPU's array and nothing in it needs to start at zero (each step
+ * writes what it reads): calls that may overlap on one GPU -- on different
+ * streams, or from several host threads -- race, so issue them on one
+ * stream.
+ */
+int pa_step_static(const pa_step_args* args, void* stream);
 
 #ifdef __cplusplus
 }

@@ -14,13 +14,15 @@ LIB_PATH = os.path.join(HERE, "libpa.so")
 
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 STATUS = {0: "PA_OK", -1: "PA_EINVAL", -2: "PA_EUNSUPPORTED", -3: "PA_EWORKSPACE",
-          -4: "PA_ELAUNCH"}
+          -4: "PA_ELAUNCH", -5: "PA_ESCRATCH"}
+PA_STATIC_SCRATCH_BYTES = 128 << 20
 
 # every symbol include/pa.h declares
 EXPORTS = ("pa_status_string", "pa_reshape_and_cache", "pa_decode_partition_size",
            "pa_decode_workspace_size", "pa_decode", "pa_decode_reduce", "pa_copy_blocks",
            "pa_mq_partition_size", "pa_mq_workspace_size", "pa_mq_attention", "pa_step",
-           "pa_step_graph_create", "pa_step_graph_launch", "pa_step_graph_destroy")
+           "pa_step_graph_create", "pa_step_graph_launch", "pa_step_graph_destroy",
+           "pa_step_static")
 
 
 class StepArgs(ctypes.Structure):
@@ -90,6 +92,8 @@ def load() -> ctypes.CDLL:
     lib.pa_step_graph_launch.argtypes = [vp, vp]
     lib.pa_step_graph_destroy.restype = i32
     lib.pa_step_graph_destroy.argtypes = [vp]
+    lib.pa_step_static.restype = i32
+    lib.pa_step_static.argtypes = [sp, vp]
     _lib = lib
     return lib
 

@@ -101,6 +101,7 @@ const char* pa_status_string(int status) {
     case PA_EUNSUPPORTED: return "unsupported shape or dtype";
     case PA_EWORKSPACE: return "workspace missing or too small";
     case PA_ELAUNCH: return "kernel launch failed";
+    case PA_ESCRATCH: return "the step needs more scratch than the static array holds";
     default: return "unknown status";
   }
 }

@@ -273,6 +273,13 @@ class Step:
         _lib.check("pa_step", _lib.load().pa_step(ctypes.byref(self.args), _stream()))
         return self.out
 
+    def run_static(self):
+        """Enqueue the step through pa_step_static (scratch in the library's
+        static per-GPU array; this object's workspace is not used)."""
+        _lib.check("pa_step_static",
+                   _lib.load().pa_step_static(ctypes.byref(self.args), _stream()))
+        return self.out
+
     def capture(self, stream):
         """Capture the step on ``stream`` (a torch.cuda.Stream, not the
         default stream) into a HIP graph."""

@@ -239,3 +239,20 @@ def test_mq_partition_choice_is_a_multiple_of_block_size():
         for B, T, q, L in ((512, 2560, 5, 1024), (64, 575, 512, 4096), (4, 8192, 2048, 2048)):
             P = pa.mq_partition_size(B, T, q, 8, 4, 256, bs, L)
             assert P >= 0 and P % bs == 0
+
+
+def test_static_step_refuses_oversize_before_any_gpu_call():
+    """pa_step_static compares the step's scratch need with its static array
+    before touching the GPU: an oversize request returns PA_ESCRATCH (-5)
+    here, with no device present."""
+    lib = _lib.load()
+    a = _lib.StepArgs()
+    a.out = a.q = a.k_cache = a.v_cache = a.block_tables = a.context_lens = FAKE
+    a.num_seqs, a.num_heads, a.num_kv_heads, a.head_dim = 33, 32, 4, 256
+    a.block_size, a.num_blocks, a.max_blocks_per_seq = 16, 100, 8192
+    a.max_context_len, a.partition_size = 131072, 16
+    a.scale, a.dtype = 0.125, _lib.PA_BF16
+    assert pa.workspace_size(33, 32, 256, 131072, 16) > _lib.PA_STATIC_SCRATCH_BYTES
+    assert lib.pa_step_static(ctypes.byref(a), None) == -5
+    assert lib.pa_step_static(None, None) == -1
+    assert pa.status_string(-5) not in ("ok", "unknown status")
