@@ -569,6 +569,43 @@ def main():
                  "unit": "GB/s"}
         print(f"[bench] graph replay: {g_ms*1e3:.1f} us/step", file=sys.stderr, flush=True)
 
+    # a model's worth of layer steps (LAYERS of them, on these buffers)
+    # eagerly, one pa_step each, against one graph holding all of them
+    layers = None
+    if not args.no_graph:
+        n_l = 8
+        lsteps = [pa.Step(q, kc, vc, bt, cl, case.scale, case.softcap, case.window,
+                          partition_size=P, max_context_len=maxL, key=key, value=value,
+                          slot_mapping=slots) for _ in range(n_l)]
+        gstream = torch.cuda.Stream()
+        lg = pa.StepGraph(lsteps, gstream)
+        reps_l = max(1, args.steps // n_l)
+        with torch.cuda.stream(gstream):
+            for _ in range(max(1, args.warmup // n_l)):
+                lg.replay(gstream)
+                for st_l in lsteps:
+                    st_l.run()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps_l):
+                for st_l in lsteps:
+                    st_l.run()
+            torch.cuda.synchronize()
+            e_us = (time.perf_counter() - t0) * 1e6 / (reps_l * n_l)
+            t0 = time.perf_counter()
+            for _ in range(reps_l):
+                lg.replay(gstream)
+            torch.cuda.synchronize()
+            g_us = (time.perf_counter() - t0) * 1e6 / (reps_l * n_l)
+        lg.close()
+        del lsteps
+        layers = {"layers": n_l, "eager_us_per_layer_step": round(e_us, 2),
+                  "graph_us_per_layer_step": round(g_us, 2),
+                  "note": f"{n_l} layer steps on these buffers: {n_l} pa_step calls against one "
+                          "graph replay holding all of them"}
+        print(f"[bench] {n_l} layer steps: eager {e_us:.1f} us/step, one graph {g_us:.1f} us/step",
+              file=sys.stderr, flush=True)
+
     if args.calib_copy_mib:
         calibration_copy(args.calib_copy_mib, dev)
 
@@ -649,6 +686,7 @@ def main():
                         "value": round(ab["total"] / (ms_step3 / 1e3) / 1e9, 2), "unit": "GB/s",
                         "note": "reshape_and_cache, pa_decode, pa_decode_reduce as separate calls"},
         "graph_replay": graph,
+        "graph_layers": layers,
         "partition_sweep": sweep,
         "cold": cold,
         "cpu_baseline": cpu,

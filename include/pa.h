@@ -298,7 +298,20 @@ typedef struct pa_step_graph pa_step_graph; /* opaque */
  */
 int pa_step_graph_create(const pa_step_args* args, void* stream, pa_step_graph** graph);
 
-/* Enqueues one replay of the captured step on `stream`. */
+/*
+ * Captures num_steps layer-steps, args[0] .. args[num_steps - 1] in this
+ * order, into one graph, e.g. the attention of every layer of a model for
+ * one decode step: a replay then runs them all from one launch, so the
+ * per-launch cost of a graph is paid once for all of them.  The steps run
+ * one after another on the stream, as the same pa_step calls would; each
+ * needs its own workspace unless they run strictly in order (they do: a
+ * graph replays them in capture order).  Arguments, errors and ownership as
+ * pa_step_graph_create (which is this call with num_steps = 1).
+ */
+int pa_step_graph_create_n(const pa_step_args* args, int num_steps, void* stream,
+                           pa_step_graph** graph);
+
+/* Enqueues one replay of the captured step(s) on `stream`. */
 int pa_step_graph_launch(pa_step_graph* graph, void* stream);
 
 /* Frees the graph (NULL is a no-op). */

@@ -21,8 +21,8 @@ PA_STATIC_SCRATCH_BYTES = 128 << 20
 EXPORTS = ("pa_status_string", "pa_reshape_and_cache", "pa_decode_partition_size",
            "pa_decode_workspace_size", "pa_decode", "pa_decode_reduce", "pa_copy_blocks",
            "pa_mq_partition_size", "pa_mq_workspace_size", "pa_mq_attention", "pa_step",
-           "pa_step_graph_create", "pa_step_graph_launch", "pa_step_graph_destroy",
-           "pa_step_static")
+           "pa_step_graph_create", "pa_step_graph_create_n", "pa_step_graph_launch",
+           "pa_step_graph_destroy", "pa_step_static")
 
 
 class StepArgs(ctypes.Structure):
@@ -88,6 +88,8 @@ def load() -> ctypes.CDLL:
     lib.pa_step.argtypes = [sp, vp]
     lib.pa_step_graph_create.restype = i32
     lib.pa_step_graph_create.argtypes = [sp, vp, ctypes.POINTER(ctypes.c_void_p)]
+    lib.pa_step_graph_create_n.restype = i32
+    lib.pa_step_graph_create_n.argtypes = [sp, i32, vp, ctypes.POINTER(ctypes.c_void_p)]
     lib.pa_step_graph_launch.restype = i32
     lib.pa_step_graph_launch.argtypes = [vp, vp]
     lib.pa_step_graph_destroy.restype = i32

@@ -580,6 +580,15 @@ static int mq_row_blocks(int head_dim, int G, int max_query_len) {
   return nr;
 }
 
+// Row blocks per wavefront of the workgroup-shared kernel: two at head_dim
+// 64 when a sequence has 256+ rows, else one, so that more workgroups stay
+// resident (measured on the 4 x 2048-token prefill at head_dim 64: 138 us
+// with two blocks against 147-149 with one; at head_dim 256 two blocks take
+// the 512-token prompt chunk from 71 to 140 us).
+static int mq_wg_row_blocks(int head_dim, int G, int max_query_len) {
+  return head_dim == 64 && (long)max_query_len * G >= 256 ? 2 : 1;
+}
+
 // Tiles of R rows over every sequence's n * G rows: at most one partial tile
 // per sequence, and never more tiles than rows.
 static long mq_max_tiles(int num_seqs, int num_tokens, int G, int R) {
@@ -608,7 +617,7 @@ int pa_mq_partition_size(int num_seqs, int num_tokens, int max_query_len, int nu
   if (mq_tiled(dtype, block_size, max_query_len)) {
     int nr = mq_row_blocks(head_dim, G, max_query_len);
     const bool wg = (long)max_query_len * G > 16L * nr;
-    if (wg) nr = 1;
+    if (wg) nr = mq_wg_row_blocks(head_dim, G, max_query_len);
     const int R = wg ? 64 * nr : 16 * nr;
     units = mq_max_tiles(num_seqs, num_tokens, G, R) * num_kv_heads;
   } else {
@@ -686,10 +695,7 @@ int pa_mq_attention(void* out, void* workspace, size_t workspace_bytes, const vo
   const int wg_env = env_int("PA_MQ_WG", -1);
   const bool wg = tiled && (wg_env >= 0 ? wg_env != 0
                                         : (long)max_query_len * G > 16L * nr);
-  // the shared kernel takes one row block per wavefront: more workgroups
-  // stay resident (measured on a 2048-token prefill at head_dim 64: 182 us
-  // with one block, 189 with two, 245 with four)
-  if (wg && nr_env == 0) nr = 1;
+  if (wg && nr_env == 0) nr = mq_wg_row_blocks(head_dim, G, max_query_len);
   const int R = wg ? 64 * nr : 16 * nr;
   pa::mq_plan_kernel<<<dim3(1), dim3(1024), 0, s>>>(
       query_start, context_lens, num_seqs, num_tokens, max_context_len, G, R,

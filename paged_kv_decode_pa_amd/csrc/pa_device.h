@@ -60,6 +60,10 @@ __device__ __forceinline__ void ld16_buf_to_lds(rsrc_t r, void* lds, uint32_t vo
                                            (int)voff, (int)soff, 0, 2);
 }
 
+// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float f16_lo(uint32_t w) {

@@ -13,11 +13,17 @@ struct pa_step_graph {
 extern "C" {
 
 int pa_step_graph_create(const pa_step_args* a, void* stream, pa_step_graph** out) {
-  if (!a || !out || !stream) return PA_EINVAL;  // capture needs a created stream
+  return pa_step_graph_create_n(a, 1, stream, out);
+}
+
+int pa_step_graph_create_n(const pa_step_args* a, int num_steps, void* stream,
+                           pa_step_graph** out) {
+  if (!a || num_steps < 1 || !out || !stream) return PA_EINVAL;  // capture needs a created stream
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) != hipSuccess)
     return PA_ELAUNCH;
-  const int st = pa_step(a, stream);
+  int st = PA_OK;
+  for (int i = 0; i < num_steps && st == PA_OK; ++i) st = pa_step(a + i, stream);
   hipGraph_t graph = nullptr;
   const hipError_t end = hipStreamEndCapture(s, &graph);
   if (st != PA_OK || end != hipSuccess || !graph) {
@@ -26,6 +32,13 @@ int pa_step_graph_create(const pa_step_args* a, void* stream, pa_step_graph** ou
   }
   hipGraphExec_t exec = nullptr;
   if (hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    return PA_ELAUNCH;
+  }
+  // move the executable graph's resources to the device now, so the first
+  // replay does not pay for it
+  if (hipGraphUpload(exec, s) != hipSuccess) {
+    (void)hipGraphExecDestroy(exec);
     (void)hipGraphDestroy(graph);
     return PA_ELAUNCH;
   }

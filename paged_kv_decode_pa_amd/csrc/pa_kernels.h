@@ -243,7 +243,7 @@ __global__ __launch_bounds__(64 * kMaxWaves, PA_DECODE_MIN_WAVES) void decode_ke
   const int nw = blockDim.x >> 6;
 
   // per-wavefront LDS, sized by the launch (decode_lds_bytes)
-  extern __shared__ float smem[];
+  extern __shared__ __align__(16) float smem[];
   float* s_wave = smem + w * S::LDS_FLOATS;
   float* sc = s_wave;                              // [SLOTS] logits / probabilities
   float* s_alpha = sc + SLOTS;                     // [G] rescale of this chunk

@@ -63,9 +63,6 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)lo, (__bf16)hi});
 }
 
-// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // Chunks in flight per wavefront.  Measured on the long-context workload:
 // 2 -> 153 us, 3 -> 160 us, 4 -> 175 us (each extra V buffer costs LDS and
@@ -82,12 +79,15 @@ struct MfmaShape {
   static constexpr int VBYTES = NT * D * 2;         // V chunk in LDS
   static constexpr int VLOADS = VBYTES / 1024;      // 1 KB direct-to-LDS loads
   static constexpr int DEPTH = PA_MFMA_DEPTH;       // chunks in flight per wavefront
-  // LDS floats per wavefront: DEPTH V chunks, block-table window, max/sum, acc
+  // LDS floats per wavefront: DEPTH V chunks, block-table window, max/sum,
+  // and the accumulators staged for a merge -- in the V buffers when they
+  // fit there (the merge comes after the last chunk's reads)
   static constexpr int V_F = DEPTH * VBYTES / 4;
   static constexpr int TBL = V_F;
   static constexpr int ML = TBL + 64;
-  static constexpr int ACC = ML + 2 * G;
-  static constexpr int LDS_FLOATS = ACC + G * (D + 4);
+  static constexpr bool ACC_IN_V = V_F >= G * (D + 4);
+  static constexpr int ACC = ACC_IN_V ? 0 : ML + 2 * G;
+  static constexpr int LDS_FLOATS = ACC_IN_V ? ML + 2 * G : ACC + G * (D + 4);
   static_assert(G == 8 || G == 16, "MFMA path: 8 or 16 query heads per KV head");
   static_assert(VBYTES % 1024 == 0, "chunk must fill whole 1 KB LDS loads");
 };
@@ -128,6 +128,41 @@ __device__ __forceinline__ void vt_frag(const char* vb, int mt, int c16, int j,
   }
 }
 
+// Max and sum over the four lanes c16 + 16 j' (j' < 4) that share a row of
+// a 16x16 MFMA result, by the gfx950 lane-swap instructions: a permlane16
+// swap of a value with itself leaves each lane its own value in one result
+// and its xor-16 partner's in the other (rows of 16 lanes trade halves), a
+// permlane32 swap likewise for the xor-32 partner.  Plain VALU moves, no
+// LDS round trip.
+__device__ __forceinline__ float max4_rows(float v) {
+  const uint32_t x = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t y = __float_as_uint(v);
+  const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum4_rows(float v) {
+  const uint32_t x = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t y = __float_as_uint(v);
+  const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// acc + lo + hi of two packed 16-bit values (one packed dot with (1, 1))
+template <int DT>
+__device__ __forceinline__ float add_pair(uint32_t pk, float acc) {
+  if constexpr (DT == DT_F16)
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk),
+                                  f16x2_t{(_Float16)1.0f, (_Float16)1.0f}, acc, false);
+  else
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk),
+                                           bf16x2_t{(__bf16)1.0f, (__bf16)1.0f}, acc, false);
+}
+
 // true when any lane's alpha is below 1 (its running max moved): only then
 // do the accumulators need rescaling
 __device__ __forceinline__ bool any_rescale(float alpha) {
@@ -157,7 +192,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
   const int c16 = lane & 15;
   const int j = lane >> 4;
 
-  extern __shared__ float smem[];
+  extern __shared__ __align__(16) float smem[];
   float* s_wave = smem + w * S::LDS_FLOATS;
   char* vbuf = reinterpret_cast<char*>(s_wave);
   int32_t* tbl = reinterpret_cast<int32_t*>(s_wave + S::TBL);
@@ -322,8 +357,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
     for (int t = 0; t < TILES; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, pr[t][i]);
-    cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
-    cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
+    cmax = max4_rows(cmax);
     const float m_new = fmaxf(m_run, cmax);
     const float alpha = fast_exp2(m_run - m_new);
     float psum = 0.0f;
@@ -412,9 +446,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
 
   if constexpr (HEADS) {
     // this wavefront holds its head's whole unit: write from registers
-    float l = l_run;
-    l += shfl_xor_f(l, 16);
-    l += shfl_xor_f(l, 32);
+    const float l = sum4_rows(l_run);
     if (c16 < G) {
       const float inv = 1.0f / l;
       const size_t row = (size_t)b * Hq + (size_t)g * G + c16;
@@ -441,8 +473,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
   }
 
   // ---- epilogue: sums over the head's four lanes, then the LDS merge ----
-  l_run += shfl_xor_f(l_run, 16);
-  l_run += shfl_xor_f(l_run, 32);
+  l_run = sum4_rows(l_run);
   if (c16 < G) {
     if (j == 0) {
       s_wave[S::ML + c16] = m_run;

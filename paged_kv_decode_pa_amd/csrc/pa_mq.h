@@ -25,6 +25,8 @@
 // the decode reduce merges them (each token's context is pos + 1).
 #pragma once
 
+#include <type_traits>
+
 #include "pa_mfma.h"
 
 namespace pa {
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
   const int c16 = lane & 15;
   const int j = lane >> 4;
 
-  extern __shared__ float smem[];
+  extern __shared__ __align__(16) float smem[];
   float* s_wave = smem + w * S::LDS_FLOATS;
   char* vbuf = reinterpret_cast<char*>(s_wave);
   int32_t* tbl = reinterpret_cast<int32_t*>(s_wave + S::TBL);
@@ -545,6 +547,7 @@ struct MQWGShape {
 // 16-bit P operand and fp32 sums hold without loss of relative precision.
 // Most chunks then skip the rescale.
 constexpr float kMaxSlack = 8.0f;
+constexpr float kSlackPow = 256.0f;  // 2^kMaxSlack
 
 // K rows in LDS: 16-byte segment s of row r is stored at s ^ k_swz(r)
 template <int D>
@@ -565,7 +568,7 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15;
   const int j = lane >> 4;
-  extern __shared__ float smem[];
+  extern __shared__ __align__(16) float smem[];
   char* lds = reinterpret_cast<char*>(smem);
 
   const int Hq = p.num_heads;
@@ -688,11 +691,12 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
     }
   };
 
-  float m_run[NR], l_run[NR];
+  float m_run[NR], l_run[NR], nm[NR];
   f32x4_t acc[NR][MT];
 #pragma unroll
   for (int nb = 0; nb < NR; ++nb) {
     m_run[nb] = kNegInf;
+    nm[nb] = 0.0f;
     l_run[nb] = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -700,6 +704,10 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
 
   const int c0 = lo / NT;
   const int c1 = (hi - 1) / NT;
+  // the chunk holding the first key of this wavefront's last row: every
+  // row's first keys lie at or before it (a row's first key does not
+  // decrease with its position)
+  const int c_ref = full_lo / NT;
 #pragma unroll
   for (int k = 0; k < NBUF - 1; ++k) issue(c0 + k, lds + k * 2 * CBYTES);
   // Chunk c from buffer kb; next (chunk c - 1's buffer) takes chunk
@@ -710,8 +718,9 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
   // for every copy in flight), and kb and next are restrict, so the
   // compiler's own wait before the LDS reads does not cover the copy just
   // issued into the other buffer.
-  auto chunk = [&](int c, const char* __restrict__ kb, char* __restrict__ next)
+  auto chunk = [&](int c, const char* __restrict__ kb, char* __restrict__ next, auto capped_c)
                    __attribute__((always_inline)) {
+    constexpr bool capped = decltype(capped_c)::value;
     __builtin_amdgcn_s_waitcnt(vmcnt_only((NBUF - 2) * LPW));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -743,9 +752,8 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
       // the cap already scaled, plain ones keep the scale for the exponent's
       // fma below
       float pr[TILES][4];
-      const bool capped = p.cap_mul > 0.0f;
       const float smul = capped ? 1.0f : p.qk_mul;
-      if (capped) {
+      if constexpr (capped) {
 #pragma unroll
         for (int t = 0; t < TILES; ++t)
 #pragma unroll
@@ -756,7 +764,6 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) pr[t][i] = sc[nb][t][i];
       }
-      float cmax = kNegInf;
       if (cs < full_lo || cs + NT > full_hi) {  // keys some row of the wavefront must not see
 #pragma unroll
         for (int t = 0; t < TILES; ++t)
@@ -766,43 +773,65 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
             pr[t][i] = (pos >= a_lo[nb] && pos < a_hi[nb]) ? pr[t][i] : kNegInf;
           }
       }
+      // Probabilities against the row's reference maximum (exponent base
+      // nm = -reference; 0 for a row with no key yet).  The reference moves
+      // only when a logit passes it by more than kMaxSlack, so most chunks
+      // keep these: the exact maximum is taken (max over the chunk, then
+      // over the row's four lanes) only in the chunks that hold some row's
+      // first keys (c <= c_ref) or when a probability of this chunk exceeds
+      // 2^kMaxSlack.  Sum, accumulators and the partial's max all use the
+      // same reference, so the result is exact in real arithmetic; a row
+      // with no key keeps (-inf, 0, 0).
+      float e[TILES][4];
 #pragma unroll
       for (int t = 0; t < TILES; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, pr[t][i]);
-      cmax = fmaxf(cmax, shfl_xor_f(cmax, 16));
-      cmax = fmaxf(cmax, shfl_xor_f(cmax, 32));
-      // The row's reference maximum moves only when a logit passes it by
-      // more than kMaxSlack (and on the row's first key: -inf + slack is
-      // -inf), so most chunks skip the rescale; probabilities stay below
-      // 2^kMaxSlack, and sum, accumulators and the partial's max all use the
-      // same reference.  A row with no key yet keeps (-inf, 0, 0) and uses 0
-      // as the exponent base.
-      const float m_cand = fmaxf(m_run[nb], cmax * smul);
-      float alpha = 1.0f;
-      if (m_cand > m_run[nb] + kMaxSlack) {
-        alpha = fast_exp2(m_run[nb] - m_cand);
-        m_run[nb] = m_cand;
+        for (int i = 0; i < 4; ++i) e[t][i] = fast_exp2(__builtin_fmaf(pr[t][i], smul, nm[nb]));
+      bool exact = c <= c_ref;
+      if (!exact) {
+        float emax = e[0][0];
+#pragma unroll
+        for (int t = 0; t < TILES; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) emax = fmaxf(emax, e[t][i]);
+        exact = __builtin_amdgcn_ballot_w64(!(emax <= kSlackPow)) != 0;
       }
-      const float m_use = m_run[nb] == kNegInf ? 0.0f : m_run[nb];
-      float psum = 0.0f;
+      if (exact) {
+        float cmax = kNegInf;
 #pragma unroll
-      for (int t = 0; t < TILES; ++t)
+        for (int t = 0; t < TILES; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pr[t][i] = fast_exp2(__builtin_fmaf(pr[t][i], smul, -m_use));
-          psum += pr[t][i];
+          for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, pr[t][i]);
+        cmax = max4_rows(cmax);
+        const float m_cand = fmaxf(m_run[nb], cmax * smul);
+        float alpha = 1.0f;
+        if (m_cand > m_run[nb] + kMaxSlack) {  // (a first key: -inf + slack is -inf)
+          alpha = fast_exp2(m_run[nb] - m_cand);
+          m_run[nb] = m_cand;
+          nm[nb] = -m_cand;
+#pragma unroll
+          for (int t = 0; t < TILES; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              e[t][i] = fast_exp2(__builtin_fmaf(pr[t][i], smul, nm[nb]));
         }
-      l_run[nb] = l_run[nb] * alpha + psum;
-      if (any_rescale(alpha)) {
+        if (any_rescale(alpha)) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[nb][mt] *= alpha;
+          for (int mt = 0; mt < MT; ++mt) acc[nb][mt] *= alpha;
+        }
+        l_run[nb] *= alpha;
       }
+      // the row sum adds the probabilities as P.V uses them (rounded to the
+      // 16-bit type), two per packed dot
+      float psum = l_run[nb];
 #pragma unroll
       for (int t = 0; t < TILES; ++t) {
-        pk[nb][2 * t] = pack2<DT>(pr[t][0], pr[t][1]);
-        pk[nb][2 * t + 1] = pack2<DT>(pr[t][2], pr[t][3]);
+        pk[nb][2 * t] = pack2<DT>(e[t][0], e[t][1]);
+        pk[nb][2 * t + 1] = pack2<DT>(e[t][2], e[t][3]);
+        psum = add_pair<DT>(pk[nb][2 * t], psum);
+        psum = add_pair<DT>(pk[nb][2 * t + 1], psum);
       }
+      l_run[nb] = psum;
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -820,13 +849,18 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
       }
     }
   };
-  int buf = 0;
+  // the chunk loop, compiled once with and once without the soft-cap
+  auto walk = [&](auto capped_c) __attribute__((always_inline)) {
+    int buf = 0;
 #pragma clang loop unroll(disable)
-  for (int c = c0; c <= c1; ++c) {
-    const int nxt = buf == 0 ? NBUF - 1 : buf - 1;
-    chunk(c, lds + buf * 2 * CBYTES, lds + nxt * 2 * CBYTES);
-    buf = buf == NBUF - 1 ? 0 : buf + 1;
-  }
+    for (int c = c0; c <= c1; ++c) {
+      const int nxt = buf == 0 ? NBUF - 1 : buf - 1;
+      chunk(c, lds + buf * 2 * CBYTES, lds + nxt * 2 * CBYTES, capped_c);
+      buf = buf == NBUF - 1 ? 0 : buf + 1;
+    }
+  };
+  if (p.cap_mul > 0.0f) walk(std::true_type{});
+  else walk(std::false_type{});
   // the copies issued past the last chunk must land before the workgroup
   // (and its LDS) goes away
   __builtin_amdgcn_s_waitcnt(0);
@@ -834,9 +868,7 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
   // ---- epilogue: each wavefront writes its own rows ----
 #pragma unroll
   for (int nb = 0; nb < NR; ++nb) {
-    float l = l_run[nb];
-    l += shfl_xor_f(l, 16);
-    l += shfl_xor_f(l, 32);
+    const float l = sum4_rows(l_run[nb]);
     const int f = fw0 + 16 * nb + c16;
     if (f >= f_end || l == 0.0f) continue;  // past the end, or no key here
     const float inv = 1.0f / l;

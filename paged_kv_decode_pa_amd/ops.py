@@ -309,3 +309,39 @@ class Step:
             self.close()
         except Exception:
             pass
+
+
+class StepGraph:
+    """Several layer steps (Step objects, e.g. one per layer of a model)
+    captured into one HIP graph on ``stream`` (a torch.cuda.Stream) and
+    replayed by one launch, in the order given (pa_step_graph_create_n)."""
+
+    def __init__(self, steps, stream):
+        if not steps:
+            raise ValueError("no steps")
+        self.steps = list(steps)
+        arr = (_lib.StepArgs * len(self.steps))(*[st.args for st in self.steps])
+        self._arr = arr
+        h = ctypes.c_void_p()
+        _lib.check("pa_step_graph_create_n", _lib.load().pa_step_graph_create_n(
+            arr, len(self.steps), stream.cuda_stream, ctypes.byref(h)))
+        self._graph = h
+
+    def replay(self, stream=None):
+        """Enqueue one replay of every captured step (on ``stream`` or
+        torch's current stream)."""
+        if self._graph is None:
+            raise RuntimeError("graph closed")
+        s = (stream or torch.cuda.current_stream()).cuda_stream
+        _lib.check("pa_step_graph_launch", _lib.load().pa_step_graph_launch(self._graph, s))
+
+    def close(self):
+        if self._graph is not None:
+            _lib.load().pa_step_graph_destroy(self._graph)
+            self._graph = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

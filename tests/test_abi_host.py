@@ -256,3 +256,15 @@ def test_static_step_refuses_oversize_before_any_gpu_call():
     assert lib.pa_step_static(ctypes.byref(a), None) == -5
     assert lib.pa_step_static(None, None) == -1
     assert pa.status_string(-5) not in ("ok", "unknown status")
+
+
+def test_graph_of_steps_refuses_bad_arguments():
+    """pa_step_graph_create_n checks its arguments before any capture: no
+    steps, a null array or a null stream is PA_EINVAL (-1)."""
+    lib = _lib.load()
+    a = (_lib.StepArgs * 1)()
+    h = ctypes.c_void_p()
+    assert lib.pa_step_graph_create_n(a, 0, FAKE, ctypes.byref(h)) == -1
+    assert lib.pa_step_graph_create_n(None, 1, FAKE, ctypes.byref(h)) == -1
+    assert lib.pa_step_graph_create_n(a, 1, None, ctypes.byref(h)) == -1
+    assert h.value is None
