@@ -458,11 +458,13 @@ def main():
             pa.decode_reduce(out, ws, cl, maxL, P, case.window)
         return e
 
-    # the whole step as one native call (pa_step): preparation launch
-    # (new rows, plan, merge counters), decode, merge
+    # the whole step as one native call (pa_step): the new rows (one per
+    # sequence at its last position, written by the decode launch itself
+    # on the vector kernel), the plan, decode, merge
+    tails = slots is not None and slots.shape[0] == B
     fused = pa.Step(q, kc, vc, bt, cl, case.scale, case.softcap, case.window,
                     partition_size=P, max_context_len=maxL, out=out, key=key, value=value,
-                    slot_mapping=slots)
+                    slot_mapping=slots, rows_at_tails=tails)
 
     def fused_step(record=False):
         fused.run()
@@ -525,7 +527,7 @@ def main():
                 continue
             st_s = pa.Step(q, kc, vc, bt, cl, case.scale, case.softcap, case.window,
                            partition_size=ps, max_context_len=maxL, key=key, value=value,
-                           slot_mapping=slots)
+                           slot_mapping=slots, rows_at_tails=tails)
             for _ in range(args.warmup):
                 st_s.run()
             torch.cuda.synchronize()
@@ -551,7 +553,7 @@ def main():
         gstream = torch.cuda.Stream()
         st = pa.Step(q, kc, vc, bt, cl, case.scale, case.softcap, case.window,
                      partition_size=P, max_context_len=maxL, out=out, key=key, value=value,
-                     slot_mapping=slots)
+                     slot_mapping=slots, rows_at_tails=tails)
         st.capture(gstream)
         with torch.cuda.stream(gstream):
             for _ in range(args.warmup):
@@ -576,7 +578,7 @@ def main():
         n_l = 8
         lsteps = [pa.Step(q, kc, vc, bt, cl, case.scale, case.softcap, case.window,
                           partition_size=P, max_context_len=maxL, key=key, value=value,
-                          slot_mapping=slots) for _ in range(n_l)]
+                          slot_mapping=slots, rows_at_tails=tails) for _ in range(n_l)]
         gstream = torch.cuda.Stream()
         lg = pa.StepGraph(lsteps, gstream)
         reps_l = max(1, args.steps // n_l)
@@ -658,6 +660,7 @@ def main():
             "context_tokens": int(case.context_lens.sum()),
             "max_context_len": maxL, "partition_size": P,
             "new_rows": 0 if slots is None else int(slots.shape[0]),
+            "new_rows_written_by": "decode launch" if tails else "preparation launch",
             "parallelism": "single GPU",
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

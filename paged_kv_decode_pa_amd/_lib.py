@@ -40,6 +40,7 @@ class StepArgs(ctypes.Structure):
         ("block_size", ctypes.c_int), ("num_blocks", ctypes.c_int),
         ("scale", ctypes.c_float), ("softcap", ctypes.c_float), ("window", ctypes.c_int),
         ("partition_size", ctypes.c_int), ("dtype", ctypes.c_int),
+        ("new_rows_at_tails", ctypes.c_int),
     ]
 
 _lib = None

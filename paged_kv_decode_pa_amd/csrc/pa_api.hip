@@ -343,8 +343,11 @@ static int decode_setup(void* out, void* workspace, size_t workspace_bytes, cons
   // costs 30% at 4 and 6% at 16); below 48 sequences the grid runs in input
   // order.  A looping launch always needs the plan's item list.
   // PA_DECODE_PLAN=0/1 overrides.
+  // A grid that runs in one round (at most one workgroup per CU) has no
+  // order to choose either.
   const int plan_env = env_int("PA_DECODE_PLAN", -1);
-  const bool need_plan = loop || (plan_env >= 0 ? plan_env != 0 : num_seqs >= 48);
+  const bool need_plan =
+      loop || (plan_env >= 0 ? plan_env != 0 : num_seqs >= 48 && blocks > kNumCUs);
   if (!need_plan) p.order = nullptr;
   // XCD-grouped grid for per-head workgroups over split keys (measured: the
   // 16-sequence sliding-window workload 57 -> 52 us; the unsplit serving
@@ -481,8 +484,22 @@ int pa_step(const pa_step_args* a, void* stream) {
                                         a->num_kv_heads, a->head_dim, a->dtype, stream)
                  : PA_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // Tail rows (one new token per sequence, at its last position): when
+  // that is all the preparation launch would do (no plan), the vector decode
+  // kernel writes them itself and the launch goes (global-layer workload,
+  // 64 sequences: step 32.1 -> 29.8 us warm, 38.8 -> 35.0 us cold; with a
+  // plan launch anyway, the serving batch lost 3 us to it).  PA_STEP_TAILS=0
+  // switches it off.
+  int T_prep = T;
+  if (a->new_rows_at_tails && T > 0 && T == a->num_seqs && !dl.mfma && !dl.need_plan &&
+      !dl.loop && env_int("PA_STEP_TAILS", 1) != 0) {
+    dl.p.tail_k = a->key;
+    dl.p.tail_v = a->value;
+    dl.p.tail_slots = a->slot_mapping;
+    T_prep = 0;
+  }
   // One launch before the decode kernel: the new K/V rows and the plan.
-  if (T > 0 || dl.need_plan) {
+  if (T_prep > 0 || dl.need_plan) {
     pa::PrepParams pp{};
     pp.context_lens = a->context_lens;
     pp.num_seqs = a->num_seqs;
@@ -496,10 +513,10 @@ int pa_step(const pa_step_args* a, void* stream) {
     pp.k_cache = static_cast<uint4*>(a->k_cache);
     pp.v_cache = static_cast<uint4*>(a->v_cache);
     pp.slot_mapping = a->slot_mapping;
-    pp.num_tokens = T;
+    pp.num_tokens = T_prep;
     pp.num_slots = (int64_t)a->num_blocks * a->block_size;
     pp.row16 = (int)((int64_t)a->num_kv_heads * a->head_dim * elem_bytes(a->dtype) / 16);
-    const long blocks = 1 + ((long)T + 3) / 4;
+    const long blocks = 1 + ((long)T_prep + 3) / 4;
     if (blocks > 0x7fffffffL) return PA_EUNSUPPORTED;
     pa::step_prep_kernel<<<dim3((unsigned)blocks), dim3(1024), 0, s>>>(pp);
     if (hipGetLastError() != hipSuccess) return PA_ELAUNCH;

@@ -57,6 +57,12 @@ struct DecodeParams {
   float cap_mul;           // > 0: logit2 = cap_mul * tanh(q.k * qk_mul)
   int xcd_units;           // > 0: XCD-grouped grid over this many (b, p) units
   int prio;                // chunks per wave-priority step (0: none)
+  // Tail rows (vector kernel): row b of tail_k / tail_v [B, Hkv, D] is the
+  // newest token of sequence b, to be written at slot tail_slots[b]; null:
+  // the caches already hold every row
+  const void* tail_k;
+  const void* tail_v;
+  const int64_t* tail_slots;
 };
 
 struct ReduceParams {
@@ -103,6 +109,7 @@ __device__ __forceinline__ const int32_t* table_row(const DecodeParams& p, int b
 // The (sequence, KV head, partition) unit of a decode workgroup.
 struct Unit {
   int b, g, part, lo, hi;
+  int L;        // the sequence's context length (clamped)
   bool single;  // the sequence's attended keys fall in this one partition
 };
 
@@ -122,6 +129,7 @@ __device__ __forceinline__ bool unit_range(const DecodeParams& p, Unit& u) {
   }
   const int P = p.part;
   const int start = p.window > 0 ? max(0, L - p.window) : 0;
+  u.L = L;
   u.lo = max(start, u.part * P);
   u.hi = min(L, u.part * P + P);
   u.single = (start / P) == ((L - 1) / P);
@@ -231,7 +239,8 @@ __device__ __forceinline__ void merge_store(const DecodeParams& p, const Unit& u
 #ifndef PA_DECODE_MIN_WAVES
 #define PA_DECODE_MIN_WAVES 1
 #endif
-template <int DT, int D, int G, bool PAGED, bool LOOP>
+// TAIL: the launch writes the new tail rows itself (p.tail_slots set).
+template <int DT, int D, int G, bool PAGED, bool LOOP, bool TAIL = false>
 __global__ __launch_bounds__(64 * kMaxWaves, PA_DECODE_MIN_WAVES) void decode_kernel(DecodeParams p) {
   using S = DecodeShape<DT, D, G>;
   constexpr int EB = S::EB, EPL = S::EPL, LPR = S::LPR, RPI = S::RPI;
@@ -402,6 +411,37 @@ __global__ __launch_bounds__(64 * kMaxWaves, PA_DECODE_MIN_WAVES) void decode_ke
     }
   }
 
+  // Tail rows (looked up after the first chunk's loads are in flight): the
+  // unit holding the sequence's newest key (position L - 1) takes that
+  // key's K/V from the new-row arrays, writes this head's slice of it to
+  // its slot (wavefront 0, after its last chunk), and, when the slot is the
+  // one the block table gives position L - 1, uses the new values wherever
+  // it would read that slot (the key itself and the rows clamped onto it) --
+  // the order reshape_and_cache-then-decode would give, with no launch in
+  // between.
+  bool tail = false, tail_store = false;
+  int64_t slot = -1;
+  uint4 k_tail = make_uint4(0, 0, 0, 0), v_tail = k_tail;
+  if (TAIL && u.hi == u.L) {
+    typedef const __attribute__((address_space(4))) int32_t cint32;
+    typedef const __attribute__((address_space(4))) int64_t cint64;
+    slot = ((cint64*)p.tail_slots)[b];
+    if (slot >= 0 && slot < ((int64_t)p.num_blocks << log2_bs)) {
+      const size_t src = ((size_t)b * Hkv * D + (size_t)g * D + e0) * EB;
+      k_tail = ld16(static_cast<const char*>(p.tail_k) + src);
+      v_tail = ld16(static_cast<const char*>(p.tail_v) + src);
+      tail_store = true;
+      const int last = u.L - 1;
+      const int phys = ((cint32*)bt)[last >> log2_bs];
+      tail = (unsigned)phys < (unsigned)p.num_blocks &&
+             slot == ((int64_t)phys << log2_bs) + (last & ((1 << log2_bs) - 1));
+    }
+  }
+  // the chunk holding position L - 1, and a row of it that reads that
+  // position: row r's position c_tail * NT + r is clamped into [lo, L - 1]
+  const int c_tail = tail ? (u.L - 1) / NT : -1;
+  auto reads_tail = [&](int i) { return max(c_tail * NT + i * RPI + rsub, lo) >= u.L - 1; };
+
 #pragma clang loop unroll(disable)
   for (; c <= c1; c += nw) {
     // issue priority from the chunks this wavefront has left, in steps of
@@ -413,6 +453,11 @@ __global__ __launch_bounds__(64 * kMaxWaves, PA_DECODE_MIN_WAVES) void decode_ke
       else if (rem >= 2 * p.prio) __builtin_amdgcn_s_setprio(2);
       else if (rem >= p.prio) __builtin_amdgcn_s_setprio(1);
       else __builtin_amdgcn_s_setprio(0);
+    }
+    if (TAIL && c == c_tail) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        if (reads_tail(i)) kr[i] = k_tail;
     }
     // q.k partial sums over this lane's slice of each row
     float dots[NV];
@@ -481,6 +526,11 @@ __global__ __launch_bounds__(64 * kMaxWaves, PA_DECODE_MIN_WAVES) void decode_ke
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // P.V
+    if (TAIL && c == c_tail) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        if (reads_tail(i)) vr[i] = v_tail;
+    }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float a = s_alpha[h];
@@ -505,6 +555,13 @@ __global__ __launch_bounds__(64 * kMaxWaves, PA_DECODE_MIN_WAVES) void decode_ke
     for (int i = 0; i < NI; ++i) vr[i] = vload(ad, i);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
+  }
+
+  // the new row's slice of this head, to its slot (no other unit reads it)
+  if (TAIL && tail_store && w == 0 && rsub == 0) {
+    const size_t dst = (size_t)slot * row_bytes + lane_bytes;
+    *reinterpret_cast<uint4*>(const_cast<char*>(kbase) + dst) = k_tail;
+    *reinterpret_cast<uint4*>(const_cast<char*>(vbase) + dst) = v_tail;
   }
 
   // ---- epilogue: finish this wavefront's sums, merge wavefronts in LDS ----

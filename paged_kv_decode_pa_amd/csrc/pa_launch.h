@@ -61,7 +61,10 @@ bool launch_mq_wg_bf16(int D, int nr, int tiles, int nbuf, dim3 grid, hipStream_
                        : (loop ? decode_kernel<DT, DV, GV, false, true>             \
                                : decode_kernel<DT, DV, GV, false, false>),          \
                  block.x, lds) == hipSuccess;                                       \
-    if (paged && loop) decode_kernel<DT, DV, GV, true, true><<<grid, block, lds, s>>>(p);   \
+    if (p.tail_slots && !loop)                                                      \
+      paged ? decode_kernel<DT, DV, GV, true, false, true><<<grid, block, lds, s>>>(p) \
+            : decode_kernel<DT, DV, GV, false, false, true><<<grid, block, lds, s>>>(p); \
+    else if (paged && loop) decode_kernel<DT, DV, GV, true, true><<<grid, block, lds, s>>>(p); \
     else if (paged) decode_kernel<DT, DV, GV, true, false><<<grid, block, lds, s>>>(p);     \
     else if (loop) decode_kernel<DT, DV, GV, false, true><<<grid, block, lds, s>>>(p);      \
     else decode_kernel<DT, DV, GV, false, false><<<grid, block, lds, s>>>(p);               \

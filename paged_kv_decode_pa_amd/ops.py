@@ -233,11 +233,14 @@ class Step:
     (if given), pa_decode and pa_decode_reduce, run through pa_step, or
     captured once into a HIP graph (``capture``) and replayed with
     ``replay``.  Buffer contents may change between runs; the tensors (and
-    so their addresses) and the host-side sizes are fixed at construction."""
+    so their addresses) and the host-side sizes are fixed at construction.
+    ``rows_at_tails``: key/value/slot_mapping have one row per sequence, row
+    i being sequence i's newest token (slot -1: none), so the decode launch
+    writes them itself."""
 
     def __init__(self, q, k_cache, v_cache, block_tables, context_lens, scale, softcap=0.0,
                  window=0, partition_size=None, max_context_len=None, out=None,
-                 key=None, value=None, slot_mapping=None):
+                 key=None, value=None, slot_mapping=None, rows_at_tails=False):
         B, Hq, D, NB, bs, Hkv = _shapes(q, k_cache, block_tables)
         _dev(q, k_cache, v_cache, block_tables, context_lens, key, value, slot_mapping)
         if max_context_len is None:
@@ -264,6 +267,8 @@ class Step:
         a.block_size, a.num_blocks = bs, NB
         a.scale, a.softcap, a.window = float(scale), float(softcap), int(window)
         a.partition_size, a.dtype = int(partition_size), _dt(q)
+        # row i of key/value is sequence i's newest token (a decode step)
+        a.new_rows_at_tails = 1 if rows_at_tails else 0
         self.args = a
         self.partition_size = int(partition_size)
         self._graph = None

@@ -38,12 +38,15 @@ class DeviceCase:
             self.slot_mapping = torch.from_numpy(case.slot_mapping).to(device)
 
 
-def run_step(dc: DeviceCase, partition_size=None, waves=None, out=None):
-    """reshape_and_cache (if the case has new rows) then decode + reduce."""
+def run_step(dc: DeviceCase, partition_size=None, waves=None, out=None, env=None):
+    """reshape_and_cache (if the case has new rows) then decode + reduce;
+    env: further library switches for this call."""
     import paged_kv_decode_pa_amd as pa
     c = dc.case
+    env = dict(env or {})
     if waves is not None:
-        os.environ["PA_DECODE_WAVES"] = str(waves)
+        env["PA_DECODE_WAVES"] = str(waves)
+    os.environ.update(env)
     try:
         if dc.slot_mapping is not None:
             pa.reshape_and_cache(dc.key, dc.value, dc.k_cache, dc.v_cache, dc.slot_mapping)
@@ -54,8 +57,8 @@ def run_step(dc: DeviceCase, partition_size=None, waves=None, out=None):
                         max_context_len=c.max_context_len, out=out)
         torch.cuda.synchronize()
     finally:
-        if waves is not None:
-            os.environ.pop("PA_DECODE_WAVES", None)
+        for k in env:
+            os.environ.pop(k, None)
     return out
 
 

@@ -61,6 +61,30 @@ def test_workload2_gemma_global_with_new_rows(P):
     say(f"workload 2 P={P}")
     c = workload(2)
     check(c, gpu(c, partition_size=P))
+    if P is None:  # the default launch runs without a plan; with one too
+        check(c, gpu(c, env={"PA_DECODE_PLAN": "1"}))
+
+
+def test_workload2_step_rows_at_tails():
+    """The global-layer step as bench.py runs it: pa_step with the new rows
+    handed over one per sequence, written by the decode launch itself (no
+    preparation launch).  Every sequence against the oracle; the caches
+    equal reshape_and_cache's bit for bit."""
+    import torch
+    import paged_kv_decode_pa_amd as pa
+    from gpu_util import DeviceCase, say, to_f64
+    say("workload 2 step, rows at tails")
+    c = workload(2)
+    assert c.slot_mapping.shape[0] == c.B
+    dc = DeviceCase(c)
+    st = pa.Step(dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, c.scale,
+                 c.softcap, c.window, max_context_len=c.max_context_len, key=dc.key,
+                 value=dc.value, slot_mapping=dc.slot_mapping, rows_at_tails=True)
+    check(c, to_f64(st.run()), want=oracle_workload(2))
+    wk, wv = oracle.reshape_and_cache(c.key, c.value, c.k_cache, c.v_cache, c.slot_mapping)
+    back = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert back(dc.k_cache).tobytes() == wk.tobytes()
+    assert back(dc.v_cache).tobytes() == wv.tobytes()
 
 
 def test_workload3_gemma_sliding_window():

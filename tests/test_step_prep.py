@@ -86,3 +86,69 @@ def test_step_matches_oracle(case):
     err = np.abs(got["1"] - want).max()
     assert err <= TOL[dt], f"max abs err {err:.3g} > {TOL[dt]}"
     assert np.array_equal(got["1"], got["0"]), "pa_step differs from the three calls"
+
+
+def _rows_per_sequence(c):
+    """The case's new rows laid out one per sequence (row i = sequence i's
+    newest token; slot -1 and zero rows for empty sequences), as a decode
+    step hands them over."""
+    live = [b for b in range(c.B) if c.context_lens[b] > 0]
+    shape = (c.B,) + c.key.shape[1:]
+    key = np.zeros(shape, dtype=c.key.dtype)
+    value = np.zeros(shape, dtype=c.value.dtype)
+    slots = np.full(c.B, -1, dtype=np.int64)
+    key[live], value[live], slots[live] = c.key, c.value, c.slot_mapping
+    return key, value, slots
+
+
+ROW_CASES = [cs for cs in CASES if cs[12]]
+
+
+@pytest.mark.parametrize("case", ROW_CASES, ids=[c[0] for c in ROW_CASES])
+def test_step_rows_at_tails(case):
+    """New rows handed over one per sequence at its last position: on the
+    vector kernel the decode launch writes them itself.  Output and caches
+    equal the three separate calls bit for bit, twice in a row, and the
+    output matches the oracle."""
+    import torch
+    import paged_kv_decode_pa_amd as pa
+    from gpu_util import TOL, DeviceCase, say, to_f64
+    name, dt, Hq, Hkv, D, bs, cap, W, P, B, (lo, hi), extra, rows, env = case
+    say(f"step rows at tails {name}")
+    rng = np.random.default_rng(sum(map(ord, name)) + 1)
+    c = make_case(B=B, Hq=Hq, Hkv=Hkv, D=D, bs=bs, dtype=dt,
+                  context_lens=_lens(rng, B, lo, hi, extra), softcap=cap, window=W,
+                  partition_size=P, seed=sum(map(ord, name)) + 11, new_rows=True,
+                  extra_table_cols=2)
+    c.key, c.value, c.slot_mapping = _rows_per_sequence(c)
+    want = oracle.decode_case(c)
+    results = {}
+    saved = {k: os.environ.get(k) for k in list(env) + ["PA_STEP_FUSE"]}
+    os.environ.update(env)
+    try:
+        for fuse in ("1", "0"):
+            os.environ["PA_STEP_FUSE"] = fuse
+            dc = DeviceCase(c)
+            step = pa.Step(dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens,
+                           c.scale, c.softcap, c.window, partition_size=P,
+                           max_context_len=c.max_context_len, key=dc.key, value=dc.value,
+                           slot_mapping=dc.slot_mapping, rows_at_tails=True)
+            first = to_f64(step.run().clone())
+            torch.cuda.synchronize()
+            second = to_f64(step.run().clone())
+            torch.cuda.synchronize()
+            assert np.array_equal(first, second), f"fuse={fuse}: second step differs"
+            bits = lambda t: t.view(torch.int32 if t.dtype == torch.float32 else torch.int16).cpu().numpy()
+            results[fuse] = (first, bits(dc.k_cache), bits(dc.v_cache))
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    out, kc, vc = results["1"]
+    assert np.isfinite(out).all(), "non-finite output"
+    assert np.abs(out - want).max() <= TOL[dt]
+    assert np.array_equal(out, results["0"][0]), "differs from the three calls"
+    assert np.array_equal(kc, results["0"][1]) and np.array_equal(vc, results["0"][2]), \
+        "caches differ from reshape_and_cache's"
