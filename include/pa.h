@@ -174,6 +174,17 @@ int pa_decode(void* out, void* workspace, size_t workspace_bytes,
               int window, int partition_size, pa_dtype dtype, void* stream);
 
 /*
+ * Measurement hook: while set, every pa_decode call made by this thread
+ * records `start_event` on its stream right before its decode kernel and
+ * `stop_event` right after it (two hipEvent_t created by the caller), so
+ * the pair brackets that one kernel -- not the plan launch before it.
+ * pa_decode returns PA_ELAUNCH if a record fails.  (NULL, NULL) clears the
+ * hook; one NULL alone is PA_EINVAL.  The library never creates or frees
+ * the events.
+ */
+int pa_set_decode_events(void* start_event, void* stop_event);
+
+/*
  * Decode attention, reduce pass: for each sequence with more than one
  * non-empty partition, combine the partials with weights
  * exp_sum_p * 2^(max_logit_p - max_p' max_logit_p') and write `out`.  This

@@ -381,6 +381,11 @@ static int decode_setup(void* out, void* workspace, size_t workspace_bytes, cons
   return PA_OK;
 }
 
+// Events pa_decode records around its decode kernel (pa_set_decode_events),
+// per calling thread.
+static thread_local hipEvent_t tl_decode_start = nullptr;
+static thread_local hipEvent_t tl_decode_stop = nullptr;
+
 // The decode kernel of a set-up launch (the plan, if needed, already queued).
 static int decode_kernel_launch(const DecodeLaunch& dl, hipStream_t s) {
   const int D = dl.head_dim, G = dl.G;
@@ -425,7 +430,19 @@ static int decode_impl(void* out, void* workspace, size_t workspace_bytes, const
   if (dl.need_plan)
     pa::plan_kernel<<<dim3(1), dim3(1024), 0, s>>>(context_lens, num_seqs, max_context_len,
                                                   window, dl.p.part, dl.plan);
-  return decode_kernel_launch(dl, s);
+  if (tl_decode_start && !seq_row && hipEventRecord(tl_decode_start, s) != hipSuccess)
+    return PA_ELAUNCH;
+  const int rc = decode_kernel_launch(dl, s);
+  if (rc == PA_OK && tl_decode_stop && !seq_row && hipEventRecord(tl_decode_stop, s) != hipSuccess)
+    return PA_ELAUNCH;
+  return rc;
+}
+
+int pa_set_decode_events(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr)) return PA_EINVAL;
+  tl_decode_start = static_cast<hipEvent_t>(start_event);
+  tl_decode_stop = static_cast<hipEvent_t>(stop_event);
+  return PA_OK;
 }
 
 int pa_decode(void* out, void* workspace, size_t workspace_bytes, const void* q,

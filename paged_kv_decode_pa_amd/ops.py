@@ -117,6 +117,17 @@ def decode_partitions(out, workspace, q, k_cache, v_cache, block_tables, context
         float(scale), float(softcap), int(window), int(partition_size), _dt(q), _stream()))
 
 
+def set_decode_events(start=None, stop=None) -> None:
+    """Have this thread's pa_decode calls record ``start`` / ``stop``
+    (torch.cuda.Event objects, each recorded once before so that it exists)
+    right around their decode kernel; no arguments clears."""
+    if (start is None) != (stop is None):
+        raise ValueError("give both events or neither")
+    _lib.check("pa_set_decode_events", _lib.load().pa_set_decode_events(
+        start.cuda_event if start is not None else None,
+        stop.cuda_event if stop is not None else None))
+
+
 def decode_reduce(out, workspace, context_lens, max_context_len, partition_size,
                   window) -> None:
     """pa_decode_reduce: merge the partials of multi-partition sequences."""

@@ -268,3 +268,11 @@ def test_graph_of_steps_refuses_bad_arguments():
     assert lib.pa_step_graph_create_n(None, 1, FAKE, ctypes.byref(h)) == -1
     assert lib.pa_step_graph_create_n(a, 1, None, ctypes.byref(h)) == -1
     assert h.value is None
+
+
+def test_decode_events_hook_arguments():
+    """pa_set_decode_events takes both events or neither (no GPU call)."""
+    lib = _lib.load()
+    assert lib.pa_set_decode_events(FAKE, None) == -1
+    assert lib.pa_set_decode_events(None, FAKE) == -1
+    assert lib.pa_set_decode_events(None, None) == 0

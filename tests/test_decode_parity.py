@@ -306,6 +306,37 @@ def test_gqa_head_map():
         assert np.all(got[:, h, :] == h // 8 + 1)
 
 
+def test_decode_events_bracket_the_decode_kernel():
+    """With the event hook set, pa_decode records the events around its
+    decode kernel only: a positive time no longer than the whole call's
+    (plan launch included), and the same output bits as without it."""
+    import torch
+    import paged_kv_decode_pa_amd as pa
+    from gpu_util import DeviceCase, run_step, say, to_f64
+    say("decode events")
+    L = list(range(1, 1000, 17))  # 59 sequences: the plan runs before the decode kernel
+    c = make_case(B=len(L), Hq=8, Hkv=4, D=256, bs=16, dtype="bf16", context_lens=L,
+                  softcap=50.0, seed=44, partition_size=0)
+    dc = DeviceCase(c)
+    ref = to_f64(run_step(dc))
+    s = torch.cuda.current_stream()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for x in e[:2]:
+        x.record(s)
+    pa.set_decode_events(e[0], e[1])
+    try:
+        e[2].record(s)
+        got = run_step(dc)
+        e[3].record(s)
+    finally:
+        pa.set_decode_events()
+    torch.cuda.synchronize()
+    kern, call = e[0].elapsed_time(e[1]), e[2].elapsed_time(e[3])
+    assert 0.0 < kern <= call
+    assert np.array_equal(to_f64(got), ref)
+    check(c, ref)
+
+
 def test_output_guard_band_untouched():
     import torch
     from gpu_util import DeviceCase, run_step, say
