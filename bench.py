@@ -33,8 +33,13 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 # committed rocprofv3 counter summaries (HBM bytes per launch) by workload
 TRAFFIC_FILES = {
+    "2": os.path.join(ROOT, "profiles", "pa_decode_gemma2_global_b64_traffic.md"),
+    "3": os.path.join(ROOT, "profiles", "pa_decode_gemma2_sliding_b16_traffic.md"),
     "4": os.path.join(ROOT, "profiles", "pa_decode_gemma2_b512_traffic.md"),
+    "5": os.path.join(ROOT, "profiles", "pa_decode_llama_gqa8_long_b33_traffic.md"),
     "spec5": os.path.join(ROOT, "profiles", "pa_mq_gemma2_spec5_b512_traffic.md"),
+    "chunk512": os.path.join(ROOT, "profiles", "pa_mq_gemma2_chunk512_traffic.md"),
+    "prefill": os.path.join(ROOT, "profiles", "pa_mq_llama_prefill_2048x4_traffic.md"),
 }
 
 
