@@ -289,7 +289,8 @@ typedef struct {
   pa_dtype dtype;
   /* nonzero: a decode step's one new token per sequence -- num_tokens ==
      num_seqs and row i of key/value is the newest token of sequence i
-     (position context_lens[i] - 1), with slot_mapping[i] its slot or -1.
+     (position context_lens[i] - 1), with slot_mapping[i] its slot or -1
+     (-1 also for a sequence with context_lens[i] == 0, which has none).
      Then the decode launch writes the rows itself (vector kernel) and no
      launch runs before it for them.  Results are the same bits either way;
      rows that break the contract give undefined results. */

@@ -63,8 +63,9 @@ int blocks_per_cu(std::atomic<int>* slot, Query&& query) {
 
 // Wavefronts per workgroup: enough to split a partition's chunks while each
 // wavefront still streams several of them (four; a launch of fewer units
-// than CUs is latency-bound, so there down to one each: 4-sequence fp32
-// workload 9.9 -> 7.4 us per step).  PA_DECODE_WAVES overrides.
+// than CUs is latency-bound, so there down to one each: the 4-sequence fp32
+// workload's decode kernel 10.2 -> 6.6 us in rocprofv3 traces).
+// PA_DECODE_WAVES overrides.
 int waves_for(int tokens_per_part, int chunk_tokens, int units) {
   int forced = env_int("PA_DECODE_WAVES", 0);
   if (forced >= 1 && forced <= pa::kMaxWaves) return forced;
