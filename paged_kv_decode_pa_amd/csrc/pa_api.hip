@@ -733,7 +733,7 @@ int pa_mq_attention(void* out, void* workspace, size_t workspace_bytes, const vo
   if (wg && nr_env == 0) nr = mq_wg_row_blocks(head_dim, G, max_query_len);
   const int R = wg ? 64 * nr : 16 * nr;
   pa::mq_plan_kernel<<<dim3(1), dim3(1024), 0, s>>>(
-      query_start, context_lens, num_seqs, num_tokens, max_context_len, G, R,
+      query_start, context_lens, num_seqs, num_tokens, max_context_len, window, G, R,
       tiled ? tiles : nullptr, (int)mq_max_tiles(num_seqs, num_tokens, G, R), num_tiles, vctx,
       tiled ? nullptr : vrow);
   if (hipGetLastError() != hipSuccess) return PA_ELAUNCH;

@@ -151,8 +151,7 @@ bool launch_mq_wg_bf16(int D, int nr, int tiles, int nbuf, dim3 grid, hipStream_
 
 #define PA_MQ_WG_CASE(DT, DV, NRV, TV, BV)                                          \
   case ((DV * 8 + NRV) * 4 + TV) * 8 + BV:                                          \
-    mq_wg_kernel<DT, DV, NRV, TV, BV>                                               \
-        <<<grid, dim3(256), MQWGShape<DT, DV, NRV, TV, BV>::LDS_BYTES, s>>>(p);     \
+    mq_wg_kernel<DT, DV, NRV, TV, BV><<<grid, dim3(256), 0, s>>>(p); /* static LDS */ \
     return true;
 
 #define PA_DEFINE_MQ_WG_LAUNCHER(NAME, DT)                                          \

@@ -117,11 +117,13 @@ __device__ __forceinline__ void vt_frag(const char* vb, int mt, int c16, int j,
                                         uint32_t (&vv)[2 * TILES]) {
   typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
   const int d = 16 * mt + 4 * (c16 & 3);
+  // the swizzle depends on r mod 16 only: tile t's address is tile 0's
+  // plus 16 t rows
+  const char* a0 = vb + v_lds_off<D>(4 * j + (c16 >> 2), d);
 #pragma unroll
   for (int t = 0; t < TILES; ++t) {
-    const int r = 16 * t + 4 * j + (c16 >> 2);
     const i16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4*)(vb + v_lds_off<D>(r, d)));
+        (lds_i16x4*)(a0 + t * 16 * 2 * D));
     const uint2 u = __builtin_bit_cast(uint2, x);
     vv[2 * t] = u.x;
     vv[2 * t + 1] = u.y;

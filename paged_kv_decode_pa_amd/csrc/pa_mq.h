@@ -536,7 +536,6 @@ struct MQWGShape {
   static constexpr int LOADS = CBYTES / 1024;   // 1 KB loads per K or V chunk
   static constexpr int LPW = 2 * LOADS / NW;    // K + V loads per wavefront per chunk
   static constexpr int NBUF = NBUF_;              // chunk buffers (NBUF - 1 in flight)
-  static constexpr int LDS_BYTES = NBUF * 2 * CBYTES;
   static_assert(CBYTES % 1024 == 0 && (2 * LOADS) % NW == 0, "chunk shape");
 };
 
@@ -549,14 +548,33 @@ struct MQWGShape {
 constexpr float kMaxSlack = 8.0f;
 constexpr float kSlackPow = 256.0f;  // 2^kMaxSlack
 
+// f(integral_constant<K>), f(integral_constant<K + 1>), ... up to N - 1
+template <int K, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (K < N) {
+    f(std::integral_constant<int, K>{});
+    static_for<K + 1, N>(f);
+  }
+}
+
 // K rows in LDS: 16-byte segment s of row r is stored at s ^ k_swz(r)
 template <int D>
 __device__ __forceinline__ int k_swz(int r) {
   return D >= 128 ? (r & 15) : ((r >> 1) & 7);
 }
 
+// Workgroups per CU the shapes the library picks (a wavefront's rows x
+// dims at most 128, or head_dim 256 with one row block) are compiled for:
+// as many as their LDS allows, at most 4 (registers 128 per lane then).
+template <int D, int NR, int TILES, int NBUF>
+constexpr int mq_wg_min_blocks() {
+  constexpr int by_lds = 160 * 1024 / (NBUF * 2 * 16 * TILES * D * 2);
+  return (NR * D <= 128 || (D == 256 && NR == 1)) ? (by_lds < 4 ? by_lds : 4) : 1;
+}
+
 template <int DT, int D, int NR, int TILES, int NBUF_>
-__global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
+__global__ __launch_bounds__(256, (mq_wg_min_blocks<D, NR, TILES, NBUF_>())) void mq_wg_kernel(
+    MQParams p) {
   using S = MQWGShape<DT, D, NR, TILES, NBUF_>;
   constexpr int NW = S::NW, RW = S::RW, R = S::R, NT = S::NT, KS = S::KS, MT = S::MT;
   constexpr int CBYTES = S::CBYTES, LOADS = S::LOADS, LPW = S::LPW, NBUF = S::NBUF;
@@ -568,8 +586,29 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15;
   const int j = lane >> 4;
-  extern __shared__ __align__(16) float smem[];
-  char* lds = reinterpret_cast<char*>(smem);
+  // The chunk buffers, each its own LDS object.  Up to head_dim 128 the
+  // chunk loop is unrolled over them: every LDS address is then a lane
+  // offset plus a constant, and the compiler's wait before a read of one
+  // buffer counts only the copies into that one.  At head_dim 256 the lane
+  // offsets of 24 fragments would stay live in registers, so the loop takes
+  // one chunk a step, the buffers slices of one array picked at run time
+  // (the restrict pointers of each step then keep the compiler's waits to
+  // the copies into the buffer read).
+  constexpr bool kUnroll = D <= 128;
+  constexpr int kOwn = kUnroll ? 2 * CBYTES : 16;
+  __shared__ __align__(16) char lds_b0[kUnroll ? 2 * CBYTES : NBUF * 2 * CBYTES];
+  __shared__ __align__(16) char lds_b1[kOwn];
+  __shared__ __align__(16) char lds_b2[kOwn];
+  __shared__ __align__(16) char lds_b3[NBUF == 4 ? kOwn : 16];
+  static_assert(NBUF == 3 || NBUF == 4, "three or four chunk buffers");
+  auto buf = [&](auto kc) __attribute__((always_inline)) -> char* {
+    constexpr int k = decltype(kc)::value % NBUF;
+    if constexpr (!kUnroll) return lds_b0 + k * 2 * CBYTES;
+    else if constexpr (k == 0) return lds_b0;
+    else if constexpr (k == 1) return lds_b1;
+    else if constexpr (k == 2) return lds_b2;
+    else return lds_b3;
+  };
 
   const int Hq = p.num_heads;
   const int G = p.group;
@@ -596,6 +635,7 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
 
   // this wavefront's rows: f0 + RW * w + 16 nb + c16
   const int fw0 = f0 + RW * w;
+  // a row's keys [a_lo, a_hi), less the lane's key offset 4 j in a chunk
   int a_lo[NR], a_hi[NR];
   uint4 qf[NR][KS];
 #pragma unroll
@@ -605,8 +645,8 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
     const int i = act ? f / G : i_first;
     const int h = act ? f - i * G : 0;
     const int pos = L - n + i;
-    a_lo[nb] = act ? max(lo, key_lo(pos)) : 0;
-    a_hi[nb] = act ? min(hi, pos + 1) : 0;
+    a_lo[nb] = (act ? max(lo, key_lo(pos)) : 0) - 4 * j;
+    a_hi[nb] = (act ? min(hi, pos + 1) : 0) - 4 * j;
     const char* qb = static_cast<const char*>(p.q) +
                      (((size_t)(q0 + i) * Hq + (size_t)g * G + h) * D + 8 * j) * EB;
 #pragma unroll
@@ -642,21 +682,23 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
   // first LOADS are K, the rest V.  Lane l's 16 bytes land at byte
   // 1024 (q % LOADS) + 16 l of the K or V chunk: row r, stored segment
   // sg, global segment sg ^ swizzle(r).
-  int ld_row[LPW];
-  uint32_t ld_seg[LPW];
+  uint32_t ld_off[LPW];
 #pragma unroll
   for (int k = 0; k < LPW; ++k) {
     const int q = LPW * w + k;
     const int o = (q % LOADS) * 1024 + lane * 16;
     const int r = o / (2 * D);
     const int sg = (o % (2 * D)) >> 4;
-    ld_row[k] = r;
-    ld_seg[k] = head_bytes + (uint32_t)((sg ^ (q < LOADS ? k_swz<D>(r) : v_swz<D>(r))) * 16);
+    ld_off[k] = (uint32_t)r * row_bytes + head_bytes +
+                (uint32_t)((sg ^ (q < LOADS ? k_swz<D>(r) : v_swz<D>(r))) * 16);
   }
+  // The copies of chunk c: the descriptors start at the chunk's first row
+  // and end after its last key (hi - 1), so that rows past it (not yet
+  // written, or another sequence's) read as zeros: their keys are masked
+  // and their V rows then add nothing.  Rows before the first key (lo) are
+  // earlier positions of the sequence, finite, and masked too.
   auto issue = [&](int c, char* kb) {
     rsrc_t kr, vr;
-    uint32_t soff = 0;
-    int rlo = 0, rhi = 0;
     if (c * NT < hi) {
       const int cs = c * NT;
       const int cpg = max(cs, lo) >> log2_bs;
@@ -671,12 +713,11 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
       }
       int phys = __builtin_amdgcn_readlane(tbl_v, cpg - pg0);
       phys = ((unsigned)phys < (unsigned)p.num_blocks) ? phys : 0;
-      const uint64_t base = (uint64_t)phys * page_bytes;
-      kr = make_rsrc(kbase + base, page_bytes);
-      vr = make_rsrc(vbase + base, page_bytes);
-      soff = (uint32_t)(cs & ((1 << log2_bs) - 1)) * row_bytes;
-      rlo = lo - cs;
-      rhi = hi - 1 - cs;
+      const uint64_t base = (uint64_t)phys * page_bytes +
+                            (uint32_t)(cs & ((1 << log2_bs) - 1)) * row_bytes;
+      const uint32_t bytes = (uint32_t)min(hi - cs, NT) * row_bytes;
+      kr = make_rsrc(kbase + base, bytes);
+      vr = make_rsrc(vbase + base, bytes);
     } else {
       kr = make_rsrc(dummy, (uint32_t)(G * D * EB));
       vr = kr;
@@ -684,10 +725,8 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
 #pragma unroll
     for (int k = 0; k < LPW; ++k) {
       const int q = LPW * w + k;
-      const int r = min(max(ld_row[k], rlo), rhi);
       const bool is_k = q < LOADS;
-      ld16_buf_to_lds(is_k ? kr : vr, kb + (is_k ? 0 : CBYTES) + (q % LOADS) * 1024,
-                      (uint32_t)r * row_bytes + ld_seg[k], soff);
+      ld16_buf_to_lds(is_k ? kr : vr, kb + (is_k ? 0 : CBYTES) + (q % LOADS) * 1024, ld_off[k], 0);
     }
   };
 
@@ -708,8 +747,9 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
   // row's first keys lie at or before it (a row's first key does not
   // decrease with its position)
   const int c_ref = full_lo / NT;
-#pragma unroll
-  for (int k = 0; k < NBUF - 1; ++k) issue(c0 + k, lds + k * 2 * CBYTES);
+  static_for<0, NBUF - 1>([&](auto kc) __attribute__((always_inline)) {
+    issue(c0 + decltype(kc)::value, buf(kc));
+  });
   // Chunk c from buffer kb; next (chunk c - 1's buffer) takes chunk
   // c + NBUF - 1.  This wavefront's copies of chunk c are done at the wait;
   // the barrier makes every wavefront's copies visible and puts every
@@ -765,13 +805,14 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
           for (int i = 0; i < 4; ++i) pr[t][i] = sc[nb][t][i];
       }
       if (cs < full_lo || cs + NT > full_hi) {  // keys some row of the wavefront must not see
+        // key 16 t + 4 j + i of the chunk, against the row's bounds less cs + 4 j
+        const int klo = a_lo[nb] - cs;
+        const int khi = a_hi[nb] - cs;
 #pragma unroll
         for (int t = 0; t < TILES; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int pos = cs + 16 * t + 4 * j + i;
-            pr[t][i] = (pos >= a_lo[nb] && pos < a_hi[nb]) ? pr[t][i] : kNegInf;
-          }
+          for (int i = 0; i < 4; ++i)
+            pr[t][i] = (16 * t + i >= klo && 16 * t + i < khi) ? pr[t][i] : kNegInf;
       }
       // Probabilities against the row's reference maximum (exponent base
       // nm = -reference; 0 for a row with no key yet).  The reference moves
@@ -789,12 +830,14 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
         for (int i = 0; i < 4; ++i) e[t][i] = fast_exp2(__builtin_fmaf(pr[t][i], smul, nm[nb]));
       bool exact = c <= c_ref;
       if (!exact) {
-        float emax = e[0][0];
+        // probabilities are >= 0 (or NaN), so their bit patterns order
+        // as the values do; NaN lands above 2^kMaxSlack too
+        uint32_t emax = __float_as_uint(e[0][0]);
 #pragma unroll
         for (int t = 0; t < TILES; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) emax = fmaxf(emax, e[t][i]);
-        exact = __builtin_amdgcn_ballot_w64(!(emax <= kSlackPow)) != 0;
+          for (int i = 0; i < 4; ++i) emax = max(emax, __float_as_uint(e[t][i]));
+        exact = __builtin_amdgcn_ballot_w64(emax > __builtin_bit_cast(uint32_t, kSlackPow)) != 0;
       }
       if (exact) {
         float cmax = kNegInf;
@@ -849,14 +892,25 @@ __global__ __launch_bounds__(256) void mq_wg_kernel(MQParams p) {
       }
     }
   };
-  // the chunk loop, compiled once with and once without the soft-cap
+  // The chunk loop, compiled once with and once without the soft-cap.
   auto walk = [&](auto capped_c) __attribute__((always_inline)) {
-    int buf = 0;
+    if constexpr (kUnroll) {
 #pragma clang loop unroll(disable)
-    for (int c = c0; c <= c1; ++c) {
-      const int nxt = buf == 0 ? NBUF - 1 : buf - 1;
-      chunk(c, lds + buf * 2 * CBYTES, lds + nxt * 2 * CBYTES, capped_c);
-      buf = buf == NBUF - 1 ? 0 : buf + 1;
+      for (int c = c0; c <= c1; c += NBUF) {
+        static_for<0, NBUF>([&](auto kc) __attribute__((always_inline)) {
+          constexpr int k = decltype(kc)::value;
+          if (k == 0 || c + k <= c1)
+            chunk(c + k, buf(kc), buf(std::integral_constant<int, k + NBUF - 1>{}), capped_c);
+        });
+      }
+    } else {
+      int bi = 0;
+#pragma clang loop unroll(disable)
+      for (int c = c0; c <= c1; ++c) {
+        chunk(c, lds_b0 + bi * 2 * CBYTES, lds_b0 + (bi == 0 ? NBUF - 1 : bi - 1) * 2 * CBYTES,
+              capped_c);
+        bi = bi == NBUF - 1 ? 0 : bi + 1;
+      }
     }
   };
   if (p.cap_mul > 0.0f) walk(std::true_type{});

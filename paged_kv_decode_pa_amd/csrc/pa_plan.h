@@ -176,77 +176,97 @@ __global__ __launch_bounds__(1024) void step_prep_kernel(PrepParams pp) {
 //   vctx[tok] = context of query token tok (its position + 1, clamped to
 //   [0, max_context_len]); vrow[tok] = its sequence (per-token path);
 //   tiles = (sequence, first row) for every R rows of each sequence's
-//   n * G rows (tiled path), at most tile_cap of them: sequences with the
-//   most keys first (counting sort over 256 length buckets, when they are
-//   at most 4096), and within a sequence its last rows (the most keys)
-//   first, so the grid runs longest work first.  Null outputs are skipped.
+//   n * G rows (tiled path), at most tile_cap of them, the most work first
+//   over all sequences: a tile's work is the span of keys its rows attend
+//   to (from its first row's window start to its last row's position),
+//   bucketed into 256 levels, and a counting sort (count, then place) puts
+//   the tiles in bucket order, so the grid dispatches the longest tiles of
+//   every sequence before any short one.  Within a bucket the order is the
+//   atomics' (a tile's results do not depend on it).  Null outputs are
+//   skipped.
 __global__ __launch_bounds__(1024) void mq_plan_kernel(const int32_t* __restrict__ query_start,
                                                        const int32_t* __restrict__ context_lens,
                                                        int num_seqs, int num_tokens,
-                                                       int max_context_len, int G, int R,
-                                                       int2* tiles, int tile_cap,
+                                                       int max_context_len, int window, int G,
+                                                       int R, int2* tiles, int tile_cap,
                                                        int32_t* num_tiles, int32_t* vctx,
                                                        int32_t* vrow) {
-  constexpr int kQS = 4096;  // sequences kept in LDS (starts, order) up to this many
+  constexpr int kQS = 4096;  // sequence starts and contexts kept in LDS up to this many
   constexpr int NBK = 256;
   __shared__ int s_tmp[17];
   __shared__ int s_off[1024];
   __shared__ int s_nt[1024];
   __shared__ int s_seq[1024];
+  __shared__ int s_n[1024];
+  __shared__ int s_L[1024];
   __shared__ int s_qs[kQS + 1];
-  __shared__ int s_order[kQS];
+  __shared__ int s_cl[kQS];
   __shared__ int hist[NBK];
   const int t = threadIdx.x;
-  const bool in_lds = num_seqs + 1 <= kQS + 1;
-  if (in_lds)
+  const bool in_lds = num_seqs <= kQS;
+  if (in_lds) {
     for (int b = t; b <= num_seqs; b += blockDim.x) s_qs[b] = query_start[b];
+    for (int b = t; b < num_seqs; b += blockDim.x) s_cl[b] = context_lens[b];
+  }
   __syncthreads();
   auto qstart = [&](int b) { return in_lds ? s_qs[b] : query_start[b]; };
+  auto ctx = [&](int b) { return in_lds ? s_cl[b] : context_lens[b]; };
   if (tiles != nullptr) {
-    if (in_lds) {
-      // sequences by attended length, longest first
-      const int span = max(max_context_len, 1);
-      auto bucket = [&](int b) {
-        const int L = min(max(context_lens[b], 0), max_context_len);
-        return NBK - 1 - (int)(((long long)L * (NBK - 1)) / span);
-      };
-      if (t < NBK) hist[t] = 0;
-      __syncthreads();
-      for (int b = t; b < num_seqs; b += blockDim.x) atomicAdd(&hist[bucket(b)], 1);
-      __syncthreads();
-      {
-        int total;
-        const int off = block_exclusive_scan(t < NBK ? hist[t] : 0, s_tmp, &total);
+    const int span = max(max_context_len, 1);
+    auto bucket = [&](int n, int L, int f0) {
+      const int p_first = L - n + f0 / G;
+      const int p_last = L - n + (min(f0 + R, n * G) - 1) / G;
+      const int klo = window > 0 ? max(0, p_first + 1 - window) : 0;
+      const int work = min(max(p_last + 1 - klo, 0), span);
+      return NBK - 1 - (int)(((long long)work * (NBK - 1)) / span);
+    };
+    if (t < NBK) hist[t] = 0;
+    __syncthreads();
+    // (up to 1024 sequences the second pass reuses the first's lists)
+    const bool one = num_seqs <= (int)blockDim.x;
+    int count = 0, total = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+      for (int k0 = 0; k0 < num_seqs; k0 += blockDim.x) {
+        if (pass == 0 || !one) {
+          const int b = k0 + t;
+          int nt = 0, n = 0, L = 0;
+          if (b < num_seqs) {
+            // rows of the sequence's tokens that lie in [0, num_tokens)
+            const int q0 = min(max(qstart(b), 0), num_tokens);
+            n = min(max(qstart(b + 1) - q0, 0), num_tokens - q0);
+            nt = (n * G + R - 1) / R;
+            L = min(ctx(b), max_context_len);
+          }
+          s_off[t] = block_exclusive_scan(nt, s_tmp, &total);
+          s_nt[t] = nt;
+          s_seq[t] = b;
+          s_n[t] = n;
+          s_L[t] = L;
+          __syncthreads();
+        }
+        // a sequence's tiles from its last rows (the most keys) down
+        const int nk = min(num_seqs - k0, (int)blockDim.x);
+        expand_lists(s_off, nk, total, [&](int kk, int i, int) {
+          const int f0 = (s_nt[kk] - 1 - i) * R;
+          const int bk = bucket(s_n[kk], s_L[kk], f0);
+          if (pass == 0) {
+            atomicAdd(&hist[bk], 1);
+          } else {
+            const int idx = atomicAdd(&hist[bk], 1);
+            if (idx < tile_cap) tiles[idx] = make_int2(s_seq[kk], f0);
+          }
+        });
+        if (pass == 0) count += total;
+        __syncthreads();
+      }
+      if (pass == 0) {
+        int all;
+        const int off = block_exclusive_scan(t < NBK ? hist[t] : 0, s_tmp, &all);
         if (t < NBK) hist[t] = off;
+        __syncthreads();
       }
-      __syncthreads();
-      for (int b = t; b < num_seqs; b += blockDim.x) s_order[atomicAdd(&hist[bucket(b)], 1)] = b;
-      __syncthreads();
     }
-    int base = 0;
-    for (int k0 = 0; k0 < num_seqs; k0 += blockDim.x) {
-      const int k = k0 + t;
-      const int b = k < num_seqs ? (in_lds ? s_order[k] : k) : 0;
-      int nt = 0;
-      if (k < num_seqs) {
-        // rows of the sequence's tokens that lie in [0, num_tokens)
-        const int q0 = min(max(qstart(b), 0), num_tokens);
-        const int n = min(max(qstart(b + 1) - q0, 0), num_tokens - q0);
-        nt = (n * G + R - 1) / R;
-      }
-      int total;
-      s_off[t] = block_exclusive_scan(nt, s_tmp, &total);
-      s_nt[t] = nt;
-      s_seq[t] = b;
-      __syncthreads();
-      const int room = max(tile_cap - base, 0);
-      expand_lists(s_off, blockDim.x, min(total, room), [&](int kk, int i, int idx) {
-        tiles[base + idx] = make_int2(s_seq[kk], (s_nt[kk] - 1 - i) * R);
-      });
-      base += total;
-      __syncthreads();
-    }
-    if (t == 0) *num_tiles = min(base, tile_cap);
+    if (t == 0) *num_tiles = min(count, tile_cap);
   }
   for (int tok = t; tok < num_tokens; tok += blockDim.x) {
     // the sequence that owns tok: the last b with query_start[b] <= tok
@@ -258,7 +278,7 @@ __global__ __launch_bounds__(1024) void mq_plan_kernel(const int32_t* __restrict
     }
     const int q0 = qstart(lo);
     const int n = qstart(lo + 1) - q0;
-    const int pos = context_lens[lo] - n + (tok - q0);
+    const int pos = ctx(lo) - n + (tok - q0);
     vctx[tok] = min(max(pos + 1, 0), max_context_len);
     if (vrow != nullptr) vrow[tok] = lo;
   }
