@@ -13,7 +13,9 @@ Prints ONE JSON line.  `value` is achieved HBM bandwidth of the whole step in
 GB/s, computed from the algorithmic bytes (K/V rows of attended tokens, q,
 out, block-table entries, context lengths, new rows) over the measured step
 time.  `roofline` reports the decode kernel alone: its algorithmic bytes over
-its average HIP-event-timed duration, against the 8 TB/s HBM peak.
+its average HIP-event-timed duration, against the 8 TB/s HBM peak, and
+(`roofline.read_ceiling`) against the read bandwidth a plain streaming kernel
+reaches on the same GPU in the same run.
 `cpu_baseline` times the float64 CPU oracle on a bounded sample of the same
 workload on this host.
 """
@@ -374,8 +376,49 @@ def bench_mq(args):
         "cold": cold,
         "cpu_baseline": cpu,
     }
+    if not args.no_ceiling:
+        res["roofline"] = with_ceiling(res["roofline"], read_ceiling(pa, torch, dev))
     print(json.dumps(res), flush=True)
 
+
+
+def read_ceiling(pa, torch, dev, gib=4):
+    """Best read bandwidth (GB/s) of the library's plain streaming probe
+    (pa_read_bandwidth_probe) over ``gib`` GiB, at three grid sizes: the
+    practical ceiling next to the data sheet's HBM peak."""
+    buf = torch.empty(gib << 28, dtype=torch.float32, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    nbytes = buf.numel() * 4
+    best = (0.0, 0)
+    for grid in (4096, 8192, 16384):
+        for _ in range(2):
+            pa.read_bandwidth_probe(buf, grid, sink)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        n = 10
+        e0.record()
+        for _ in range(n):
+            pa.read_bandwidth_probe(buf, grid, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = nbytes / (e0.elapsed_time(e1) / n / 1e3) / 1e9
+        best = max(best, (gbs, grid))
+    del buf
+    torch.cuda.empty_cache()
+    return {"gbs": round(best[0], 1), "grid": best[1],
+            "probe": (f"pa_read_bandwidth_probe: one pass over {gib} GiB, 256-thread workgroups, "
+                      "16-byte non-temporal loads, 8 in flight per thread; best of grids "
+                      "4096/8192/16384, 10 launches each (HIP events)")}
+
+
+def with_ceiling(roof, ceiling):
+    """Adds the measured read ceiling to an HBM-bound roofline object."""
+    if ceiling is None or roof.get("bound") != "hbm":
+        return roof
+    roof = dict(roof)
+    roof["read_ceiling"] = dict(ceiling)
+    roof["read_ceiling"]["frac"] = round(roof["achieved"] / ceiling["gbs"], 4)
+    return roof
 
 
 def main():
@@ -402,6 +445,8 @@ def main():
                     help="skip the HIP-graph replay of the step")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the streaming-read probe that measures the practical HBM ceiling")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -715,6 +760,8 @@ def main():
         "cold": cold,
         "cpu_baseline": cpu,
     }
+    if not args.no_ceiling:
+        res["roofline"] = with_ceiling(res["roofline"], read_ceiling(pa, torch, dev))
     print(json.dumps(res), flush=True)
 
 

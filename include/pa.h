@@ -185,6 +185,19 @@ int pa_decode(void* out, void* workspace, size_t workspace_bytes,
 int pa_set_decode_events(void* start_event, void* stop_event);
 
 /*
+ * Measurement aid, not part of the attention path: one streaming pass that
+ * reads `bytes` of device memory at `buf` (16-byte aligned, a multiple of
+ * 16 bytes) with `grid` workgroups of 256 threads, 16-byte non-temporal
+ * loads, eight in flight per thread.  It gives the read bandwidth a plain
+ * kernel reaches on this GPU: the practical ceiling the memory-bound
+ * decode kernels are reported against next to the data sheet's peak.
+ * `sink` is a 4-byte device word the kernel may write (it practically never
+ * does).  Nothing is allocated; the launch is queued on `stream`.  Returns
+ * PA_EINVAL for bad arguments, PA_ELAUNCH if the launch fails.
+ */
+int pa_read_bandwidth_probe(const void* buf, size_t bytes, int grid, void* sink, void* stream);
+
+/*
  * Decode attention, reduce pass: for each sequence with more than one
  * non-empty partition, combine the partials with weights
  * exp_sum_p * 2^(max_logit_p - max_p' max_logit_p') and write `out`.  This

@@ -22,7 +22,8 @@ EXPORTS = ("pa_status_string", "pa_reshape_and_cache", "pa_decode_partition_size
            "pa_decode_workspace_size", "pa_decode", "pa_decode_reduce", "pa_copy_blocks",
            "pa_mq_partition_size", "pa_mq_workspace_size", "pa_mq_attention", "pa_step",
            "pa_step_graph_create", "pa_step_graph_create_n", "pa_step_graph_launch",
-           "pa_step_graph_destroy", "pa_step_static", "pa_set_decode_events")
+           "pa_step_graph_destroy", "pa_step_static", "pa_set_decode_events",
+           "pa_read_bandwidth_probe")
 
 
 class StepArgs(ctypes.Structure):
@@ -99,6 +100,8 @@ def load() -> ctypes.CDLL:
     lib.pa_step_static.argtypes = [sp, vp]
     lib.pa_set_decode_events.restype = i32
     lib.pa_set_decode_events.argtypes = [vp, vp]
+    lib.pa_read_bandwidth_probe.restype = i32
+    lib.pa_read_bandwidth_probe.argtypes = [vp, sz, i32, vp, vp]
     _lib = lib
     return lib
 

@@ -128,6 +128,17 @@ def set_decode_events(start=None, stop=None) -> None:
         stop.cuda_event if stop is not None else None))
 
 
+def read_bandwidth_probe(buf, grid, sink) -> None:
+    """pa_read_bandwidth_probe: one streaming read of the device tensor
+    ``buf`` (its whole storage, a multiple of 16 bytes) by ``grid``
+    workgroups, queued on torch's current stream; ``sink`` is a device
+    tensor of at least 4 bytes the kernel may write."""
+    _dev(buf, sink)
+    nbytes = buf.numel() * buf.element_size()
+    _lib.check("pa_read_bandwidth_probe", _lib.load().pa_read_bandwidth_probe(
+        buf.data_ptr(), nbytes, int(grid), sink.data_ptr(), _stream()))
+
+
 def decode_reduce(out, workspace, context_lens, max_context_len, partition_size,
                   window) -> None:
     """pa_decode_reduce: merge the partials of multi-partition sequences."""

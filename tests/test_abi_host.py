@@ -276,3 +276,14 @@ def test_decode_events_hook_arguments():
     assert lib.pa_set_decode_events(FAKE, None) == -1
     assert lib.pa_set_decode_events(None, FAKE) == -1
     assert lib.pa_set_decode_events(None, None) == 0
+
+
+def test_read_bandwidth_probe_refuses_bad_arguments():
+    """pa_read_bandwidth_probe checks its arguments before any launch."""
+    lib = _lib.load()
+    assert lib.pa_read_bandwidth_probe(None, 1 << 20, 64, FAKE, None) == -1
+    assert lib.pa_read_bandwidth_probe(FAKE, 1 << 20, 64, None, None) == -1
+    assert lib.pa_read_bandwidth_probe(FAKE, 1 << 20, 0, FAKE, None) == -1
+    assert lib.pa_read_bandwidth_probe(FAKE, 24, 64, FAKE, None) == -1     # not whole 16 B
+    assert lib.pa_read_bandwidth_probe(FAKE, 0, 64, FAKE, None) == -1
+    assert lib.pa_read_bandwidth_probe(FAKE + 8, 1 << 20, 64, FAKE, None) == -1  # misaligned
