@@ -89,6 +89,7 @@ struct MfmaShape {
   static constexpr int ACC = ACC_IN_V ? 0 : ML + 2 * G;
   static constexpr int LDS_FLOATS = ACC_IN_V ? ML + 2 * G : ACC + G * (D + 4);
   static_assert(G == 8 || G == 16, "MFMA path: 8 or 16 query heads per KV head");
+  static_assert(KS % 2 == 0, "k-steps come in pairs (whole-line K loads)");
   static_assert(VBYTES % 1024 == 0, "chunk must fill whole 1 KB LDS loads");
 };
 
@@ -128,6 +129,37 @@ __device__ __forceinline__ void vt_frag(const char* vb, int mt, int c16, int j,
     vv[2 * t] = u.x;
     vv[2 * t + 1] = u.y;
   }
+}
+
+// K fragments from whole 128-byte lines.  The A operand of q.k step s
+// wants lane (c16, j) to hold token 16t + c16, dims 32s + 8j .. +8: a load
+// shaped like that reads 64 bytes of each of 16 rows, half of each line
+// (measured on this GPU: 5.8-6.0 TB/s for that pattern against 6.7-6.9 for
+// whole lines).  Steps 2p and 2p + 1 cover line p of the rows, so their two
+// loads are taken as whole lines instead, eight rows each:
+//   load h (h = 0, 1) gives lane (c16, j) row 16t + 8h + c16 % 8, 16-byte
+//   segment 8p + j + 4 (c16 / 8 xor h) of the head's row;
+// kline_operands() then hands each lane its own row again.
+__device__ __forceinline__ void kline_rowseg(int c16, int j, int t, int s, int& row, int& seg) {
+  const int h = s & 1;
+  row = 16 * t + 8 * h + (c16 & 7);
+  seg = 8 * (s >> 1) + j + 4 * ((c16 >> 3) ^ h);
+}
+
+// The A operands of steps 2p (a0) and 2p + 1 (a1) from line p's two loads:
+// lane (c16, j) needs row c16, segments 8p + j and 8p + 4 + j.  Lanes
+// c16 < 8 find them in load 0, their own and that of lane c16 + 8; lanes
+// c16 >= 8 in load 1, their own and that of lane c16 - 8: a select, and a
+// select moved across the halves of each 16-lane row (DPP row rotate by 8).
+__device__ __forceinline__ void kline_operands(int c16, const uint4& l0, const uint4& l1, uint4& a0,
+                                               uint4& a1) {
+  const bool hi8 = (c16 & 8) != 0;
+  const uint4 x = hi8 ? l0 : l1;
+  a0 = hi8 ? l1 : l0;
+  a1.x = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.x, 0x128, 0xF, 0xF, false);
+  a1.y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.y, 0x128, 0xF, 0xF, false);
+  a1.z = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.z, 0x128, 0xF, 0xF, false);
+  a1.w = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x.w, 0x128, 0xF, 0xF, false);
 }
 
 // Max and sum over the four lanes c16 + 16 j' (j' < 4) that share a row of
@@ -278,11 +310,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
     a.rlo = 0;
     a.rhi = 0;
   };
-  // K fragment (tile t, k-step s): token 16t + c16, dims 32s + 8j
+  // K loads of tile t, k-step s, whole lines (kline_rowseg)
   auto kload = [&](const Addr& a, int t, int s) -> uint4 {
-    const int r = min(max(16 * t + c16, a.rlo), a.rhi);
-    return ld16_buf(a.kr, (uint32_t)r * row_bytes + head_bytes + (uint32_t)((32 * s + 8 * j) * EB),
-                    a.soff);
+    int row, seg;
+    kline_rowseg(c16, j, t, s, row, seg);
+    const int r = min(max(row, a.rlo), a.rhi);
+    return ld16_buf(a.kr, (uint32_t)r * row_bytes + head_bytes + (uint32_t)(seg * 16), a.soff);
   };
   auto vcopy = [&](const Addr& a, char* vb) {
 #pragma unroll
@@ -323,7 +356,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void decode_mfma_kernel(DecodeParam
     for (int t = 0; t < TILES; ++t) {
       sc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) sc[t] = mfma_k32<DT>(k[t][s], qf[s], sc[t]);
+      for (int s = 0; s < KS; s += 2) {
+        uint4 a0, a1;
+        kline_operands(c16, k[t][s], k[t][s + 1], a0, a1);
+        sc[t] = mfma_k32<DT>(a0, qf[s], sc[t]);
+        sc[t] = mfma_k32<DT>(a1, qf[s + 1], sc[t]);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     Addr an;

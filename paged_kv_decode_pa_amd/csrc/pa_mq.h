@@ -240,10 +240,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
     a.rlo = 0;
     a.rhi = 0;
   };
+  // K loads of tile t, k-step s, whole lines (kline_rowseg)
   auto kload = [&](const Addr& a, int t, int s) -> uint4 {
-    const int r = min(max(16 * t + c16, a.rlo), a.rhi);
-    return ld16_buf(a.kr, (uint32_t)r * row_bytes + head_bytes + (uint32_t)((32 * s + 8 * j) * EB),
-                    a.soff);
+    int row, seg;
+    kline_rowseg(c16, j, t, s, row, seg);
+    const int r = min(max(row, a.rlo), a.rhi);
+    return ld16_buf(a.kr, (uint32_t)r * row_bytes + head_bytes + (uint32_t)(seg * 16), a.soff);
   };
   auto vcopy = [&](const Addr& a, char* vb) {
 #pragma unroll
@@ -284,10 +286,18 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
 #pragma unroll
     for (int nb = 0; nb < NR; ++nb)
 #pragma unroll
-      for (int t = 0; t < TILES; ++t) {
-        sc[nb][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int t = 0; t < TILES; ++t) sc[nb][t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) sc[nb][t] = mfma_k32<DT>(k[t][s], qf[nb][s], sc[nb][t]);
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int s = 0; s < KS; s += 2) {
+        uint4 a0, a1;
+        kline_operands(c16, k[t][s], k[t][s + 1], a0, a1);
+#pragma unroll
+        for (int nb = 0; nb < NR; ++nb) {
+          sc[nb][t] = mfma_k32<DT>(a0, qf[nb][s], sc[nb][t]);
+          sc[nb][t] = mfma_k32<DT>(a1, qf[nb][s + 1], sc[nb][t]);
+        }
       }
     __builtin_amdgcn_sched_barrier(0);
     Addr an;
