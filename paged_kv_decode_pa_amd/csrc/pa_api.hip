@@ -633,10 +633,16 @@ static long mq_max_tiles(int num_seqs, int num_tokens, int G, int R) {
 }
 
 // Workspace: vctx [T], vrow [T], tiles [max tiles at R = 16] int32 pairs,
-// the tile count, then a decode workspace for T sequences.
-static size_t mq_head_bytes(int num_seqs, int num_tokens, int G) {
+// the tile and unit counts, (keys split) units [max tiles at R = 64 x NP]
+// int32 pairs, then a decode workspace for T sequences.
+static size_t mq_unit_cap(int num_seqs, int num_tokens, int G, int np) {
+  return np > 1 ? (size_t)mq_max_tiles(num_seqs, num_tokens, G, 64) * np : 0;
+}
+
+static size_t mq_head_bytes(int num_seqs, int num_tokens, int G, int np) {
   return 2 * pad256((size_t)num_tokens * 4) +
-         pad256((size_t)mq_max_tiles(num_seqs, num_tokens, G, 16) * 8) + 256;
+         pad256((size_t)mq_max_tiles(num_seqs, num_tokens, G, 16) * 8) + 256 +
+         pad256(mq_unit_cap(num_seqs, num_tokens, G, np) * 8);
 }
 
 int pa_mq_partition_size(int num_seqs, int num_tokens, int max_query_len, int num_heads,
@@ -671,7 +677,8 @@ size_t pa_mq_workspace_size(int num_seqs, int num_tokens, int num_heads, int num
   if (num_seqs <= 0 || num_tokens <= 0 || num_heads <= 0 || num_kv_heads <= 0 ||
       num_heads % num_kv_heads || head_dim <= 0 || partition_size < 0)
     return 0;
-  return mq_head_bytes(num_seqs, num_tokens, num_heads / num_kv_heads) +
+  return mq_head_bytes(num_seqs, num_tokens, num_heads / num_kv_heads,
+                       num_parts(max_context_len, partition_size)) +
          pa_decode_workspace_size(num_tokens, num_heads, head_dim, max_context_len,
                                   partition_size);
 }
@@ -717,8 +724,11 @@ int pa_mq_attention(void* out, void* workspace, size_t workspace_bytes, const vo
   int32_t* num_tiles = reinterpret_cast<int32_t*>(
       wsb + 2 * pad256((size_t)num_tokens * 4) +
       pad256((size_t)mq_max_tiles(num_seqs, num_tokens, G, 16) * 8));
-  char* dws = wsb + mq_head_bytes(num_seqs, num_tokens, G);
-  const size_t dws_bytes = workspace_bytes - mq_head_bytes(num_seqs, num_tokens, G);
+  const int np = num_parts(max_context_len, partition_size);
+  int2* units = reinterpret_cast<int2*>(reinterpret_cast<char*>(num_tiles) + 256);
+  const size_t head = mq_head_bytes(num_seqs, num_tokens, G, np);
+  char* dws = wsb + head;
+  const size_t dws_bytes = workspace_bytes - head;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   // More rows per (sequence, KV head) than one wavefront holds: the
@@ -732,10 +742,19 @@ int pa_mq_attention(void* out, void* workspace, size_t workspace_bytes, const vo
                                         : (long)max_query_len * G > 16L * nr);
   if (wg && nr_env == 0) nr = mq_wg_row_blocks(head_dim, G, max_query_len);
   const int R = wg ? 64 * nr : 16 * nr;
+  // keys split on the shared kernel: its grid walks the plan's sorted
+  // (tile, partition) list (PA_MQ_UNITS=0: tiles in plan order, partitions
+  // slowest)
+  const bool by_units = wg && np > 1 && env_int("PA_MQ_UNITS", 1) != 0;
+  const bool split = partials_bytes(num_tokens, num_heads, head_dim, max_context_len,
+                                    partition_size) != 0;
   pa::mq_plan_kernel<<<dim3(1), dim3(1024), 0, s>>>(
       query_start, context_lens, num_seqs, num_tokens, max_context_len, window, G, R,
-      tiled ? tiles : nullptr, (int)mq_max_tiles(num_seqs, num_tokens, G, R), num_tiles, vctx,
-      tiled ? nullptr : vrow);
+      tiled ? tiles : nullptr, (int)mq_max_tiles(num_seqs, num_tokens, G, R), num_tiles,
+      partition_size, by_units ? units : nullptr,
+      (int)mq_unit_cap(num_seqs, num_tokens, G, np),
+      // token contexts: the per-token path's sequences, or the reduce's rows
+      !tiled || split ? vctx : nullptr, tiled ? nullptr : vrow);
   if (hipGetLastError() != hipSuccess) return PA_ELAUNCH;
 
   int rc;
@@ -746,7 +765,6 @@ int pa_mq_attention(void* out, void* workspace, size_t workspace_bytes, const vo
                      block_size, num_blocks, scale, softcap, window, partition_size, dtype,
                      stream, vrow);
   } else {
-    const int np = num_parts(max_context_len, partition_size);
     pa::MQParams p{};
     p.out = out;
     if (partials_bytes(num_tokens, num_heads, head_dim, max_context_len, partition_size)) {
@@ -759,6 +777,7 @@ int pa_mq_attention(void* out, void* workspace, size_t workspace_bytes, const vo
     }
     p.tiles = tiles;
     p.num_tiles = num_tiles;
+    p.units = by_units ? units : nullptr;
     p.q = q;
     p.k_cache = k_cache;
     p.v_cache = v_cache;

@@ -37,7 +37,8 @@ struct MQParams {
   float* max_logits;          // [T, Hq, NP], base-2 logits
   float* exp_sums;            // [T, Hq, NP]
   const int2* tiles;          // (sequence, first row) of each tile
-  const int32_t* num_tiles;   // [1]
+  const int32_t* num_tiles;   // [2]: tiles, units
+  const int2* units;          // (tile, partition) per grid unit, or null
   const void* q;              // [T, Hq, D]
   const void* k_cache;        // [NB, bs, Hkv, D]
   const void* v_cache;
@@ -622,11 +623,22 @@ __global__ __launch_bounds__(256, (mq_wg_min_blocks<D, NR, TILES, NBUF_>())) voi
 
   const int Hq = p.num_heads;
   const int G = p.group;
+  // unit: KV head fastest, then the plan's (tile, partition) list, or
+  // without one tiles in plan order with partitions slowest
   const int g = blockIdx.x % p.num_kv_heads;
   const int rest = blockIdx.x / p.num_kv_heads;
-  const int tile = rest % p.max_tiles;
-  const int part = rest / p.max_tiles;
-  if (tile >= *(cint32*)p.num_tiles) return;
+  int tile, part;
+  if (p.units != nullptr) {
+    if (rest >= ((cint32*)p.num_tiles)[1]) return;
+    const uint64_t u = ((cu64*)p.units)[rest];
+    tile = (int)(uint32_t)u;
+    part = (int)(uint32_t)(u >> 32);
+    if (tile >= *(cint32*)p.num_tiles) return;
+  } else {
+    tile = rest % p.max_tiles;
+    part = rest / p.max_tiles;
+    if (tile >= *(cint32*)p.num_tiles) return;
+  }
   const uint64_t tl = ((cu64*)p.tiles)[tile];
   const int b = (int)(uint32_t)tl;
   const int f0 = (int)(uint32_t)(tl >> 32);

@@ -26,20 +26,44 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_tmp, int* tota
   }
   if (lane == 63) s_tmp[w] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int k = 0; k < (int)(blockDim.x >> 6); ++k) {
-      const int t = s_tmp[k];
-      s_tmp[k] = run;
-      run += t;
+  if (w == 0) {
+    // wavefront 0 scans the (at most 16) wavefront sums
+    const int nw = (int)(blockDim.x >> 6);
+    const int y = lane < nw ? s_tmp[lane] : 0;
+    int z = y;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int u = __shfl_up(z, d, 64);
+      if (lane >= d) z += u;
     }
-    s_tmp[16] = run;
+    if (lane < nw) s_tmp[lane] = z - y;
+    if (lane == nw - 1) s_tmp[16] = z;
   }
   __syncthreads();
   const int r = x - v + s_tmp[w];
   *total = s_tmp[16];
   __syncthreads();
   return r;
+}
+
+// Exclusive prefix sum of h[0, 256) in place by one wavefront (4 entries a
+// lane); returns the sum.  The caller brackets it with workgroup barriers.
+__device__ __forceinline__ int wave_scan_256(int* h) {
+  const int lane = threadIdx.x & 63;
+  const int a = h[4 * lane], b = h[4 * lane + 1], c = h[4 * lane + 2], d = h[4 * lane + 3];
+  const int own = a + b + c + d;
+  int z = own;
+#pragma unroll
+  for (int k = 1; k < 64; k <<= 1) {
+    const int u = __shfl_up(z, k, 64);
+    if (lane >= k) z += u;
+  }
+  const int base = z - own;
+  h[4 * lane] = base;
+  h[4 * lane + 1] = base + a;
+  h[4 * lane + 2] = base + a + b;
+  h[4 * lane + 3] = base + a + b + c;
+  return __shfl(z, 63, 64);
 }
 
 // Expands nk lists into one array of `total` entries, all threads writing:
@@ -78,17 +102,15 @@ __device__ __forceinline__ void plan_body(const int32_t* __restrict__ context_le
   // counting sort over 256 length buckets, descending: the longest
   // sequences land in bucket 0 (order within a bucket is arbitrary, which
   // no result depends on)
+  // (float scaling: only the order matters, and it is monotonic)
+  const float inv_span = (float)(NBK - 1) / (float)span;
   auto bucket = [&](int L) {
     const int n = window > 0 ? min(L, window) : L;
-    return NBK - 1 - (int)(((long long)n * (NBK - 1)) / span);
+    return NBK - 1 - min(NBK - 1, (int)((float)n * inv_span));
   };
   for (int b = t; b < num_seqs; b += blockDim.x) atomicAdd(&hist[bucket(length(b))], 1);
   __syncthreads();
-  {
-    int total;
-    const int off = block_exclusive_scan(t < NBK ? hist[t] : 0, s_tmp, &total);
-    if (t < NBK) hist[t] = off;
-  }
+  if (t < 64) wave_scan_256(hist);
   __syncthreads();
   for (int b = t; b < num_seqs; b += blockDim.x)
     plan.order[atomicAdd(&hist[bucket(length(b))], 1)] = b;
@@ -182,15 +204,25 @@ __global__ __launch_bounds__(1024) void step_prep_kernel(PrepParams pp) {
 //   bucketed into 256 levels, and a counting sort (count, then place) puts
 //   the tiles in bucket order, so the grid dispatches the longest tiles of
 //   every sequence before any short one.  Within a bucket the order is the
-//   atomics' (a tile's results do not depend on it).  Null outputs are
-//   skipped.
+//   atomics' (a tile's results do not depend on it).
+//   units = (tile, partition) for every partition of part_size keys that a
+//   tile's key span meets (keys split), sorted the same way by their work
+//   (the keys the pair covers times the wavefronts, of the four R / 4-row
+//   ones, that hold rows of the tile), and their count in num_tiles[1].  A
+//   launch over this list holds no empty units, and consecutive workgroups
+//   carry similar work: the dispatcher deals them to the shader engines of
+//   an XCD in turn (stalling when the next one is full) and to an engine's
+//   CUs in turn, so each run of 256 workgroups puts one on every CU and the
+//   heaviest units spread evenly.
+//   Null outputs are skipped (vctx and vrow together skip the token loop).
 __global__ __launch_bounds__(1024) void mq_plan_kernel(const int32_t* __restrict__ query_start,
                                                        const int32_t* __restrict__ context_lens,
                                                        int num_seqs, int num_tokens,
                                                        int max_context_len, int window, int G,
                                                        int R, int2* tiles, int tile_cap,
-                                                       int32_t* num_tiles, int32_t* vctx,
-                                                       int32_t* vrow) {
+                                                       int32_t* num_tiles, int part_size,
+                                                       int2* units, int unit_cap,
+                                                       int32_t* vctx, int32_t* vrow) {
   constexpr int kQS = 4096;  // sequence starts and contexts kept in LDS up to this many
   constexpr int NBK = 256;
   __shared__ int s_tmp[17];
@@ -202,6 +234,7 @@ __global__ __launch_bounds__(1024) void mq_plan_kernel(const int32_t* __restrict
   __shared__ int s_qs[kQS + 1];
   __shared__ int s_cl[kQS];
   __shared__ int hist[NBK];
+  __shared__ int uhist[NBK];
   const int t = threadIdx.x;
   const bool in_lds = num_seqs <= kQS;
   if (in_lds) {
@@ -213,18 +246,45 @@ __global__ __launch_bounds__(1024) void mq_plan_kernel(const int32_t* __restrict
   auto ctx = [&](int b) { return in_lds ? s_cl[b] : context_lens[b]; };
   if (tiles != nullptr) {
     const int span = max(max_context_len, 1);
-    auto bucket = [&](int n, int L, int f0) {
+    const int P = part_size;
+    // the keys a tile's rows attend to: [klo, khi)
+    auto keys_of = [&](int n, int L, int f0, int& klo, int& khi) {
       const int p_first = L - n + f0 / G;
-      const int p_last = L - n + (min(f0 + R, n * G) - 1) / G;
-      const int klo = window > 0 ? max(0, p_first + 1 - window) : 0;
-      const int work = min(max(p_last + 1 - klo, 0), span);
-      return NBK - 1 - (int)(((long long)work * (NBK - 1)) / span);
+      khi = L - n + (min(f0 + R, n * G) - 1) / G + 1;
+      klo = window > 0 ? max(0, p_first + 1 - window) : 0;
+    };
+    // 256 levels of work, the most in bucket 0 (float scaling: only the
+    // order matters, and it is monotonic)
+    const float inv_span = (float)(NBK - 1) / (float)span;
+    // a unit's work: keys x wavefronts holding rows (of four, R / 4 rows each)
+    const float inv_part = P > 0 ? (float)(NBK - 1) / (float)(4 * P) : 0.0f;
+    const int rw = max(R >> 2, 1);
+    auto bucket = [&](int work, float inv) {
+      return NBK - 1 - min(NBK - 1, (int)((float)max(work, 0) * inv));
+    };
+    // a tile's units: the partitions [pf, pl] its keys meet, bucketed by
+    // their work; f(part, count, bucket) takes `count` partitions from `part`
+    // on (the whole ones between the first and the last, P keys each, in one
+    // call)
+    auto for_units = [&](int klo, int khi, int rows, auto&& f) {
+      if (khi <= klo) return;
+      const int w = min((rows + rw - 1) / rw, 4);
+      const int pf = klo / P;
+      const int pl = (khi - 1) / P;
+      if (pf == pl) {
+        f(pf, 1, bucket((khi - klo) * w, inv_part));
+        return;
+      }
+      f(pf, 1, bucket((pf * P + P - klo) * w, inv_part));
+      if (pl - pf > 1) f(pf + 1, pl - pf - 1, bucket(P * w, inv_part));
+      f(pl, 1, bucket((khi - pl * P) * w, inv_part));
     };
     if (t < NBK) hist[t] = 0;
+    if (t < NBK) uhist[t] = 0;
     __syncthreads();
     // (up to 1024 sequences the second pass reuses the first's lists)
     const bool one = num_seqs <= (int)blockDim.x;
-    int count = 0, total = 0;
+    int count = 0, total = 0, nu = 0;
     for (int pass = 0; pass < 2; ++pass) {
       for (int k0 = 0; k0 < num_seqs; k0 += blockDim.x) {
         if (pass == 0 || !one) {
@@ -248,26 +308,45 @@ __global__ __launch_bounds__(1024) void mq_plan_kernel(const int32_t* __restrict
         const int nk = min(num_seqs - k0, (int)blockDim.x);
         expand_lists(s_off, nk, total, [&](int kk, int i, int) {
           const int f0 = (s_nt[kk] - 1 - i) * R;
-          const int bk = bucket(s_n[kk], s_L[kk], f0);
+          int klo, khi;
+          keys_of(s_n[kk], s_L[kk], f0, klo, khi);
+          const int bk = bucket(khi - klo, inv_span);
+          const int rows = min(R, s_n[kk] * G - f0);
           if (pass == 0) {
             atomicAdd(&hist[bk], 1);
+            if (units != nullptr)
+              for_units(klo, khi, rows, [&](int, int c, int ub) { atomicAdd(&uhist[ub], c); });
           } else {
             const int idx = atomicAdd(&hist[bk], 1);
-            if (idx < tile_cap) tiles[idx] = make_int2(s_seq[kk], f0);
+            if (idx < tile_cap) {
+              tiles[idx] = make_int2(s_seq[kk], f0);
+              if (units != nullptr)
+                for_units(klo, khi, rows, [&](int part, int c, int ub) {
+                  const int u = atomicAdd(&uhist[ub], c);
+                  for (int k = 0; k < c && u + k < unit_cap; ++k)
+                    units[u + k] = make_int2(idx, part + k);
+                });
+            }
           }
         });
         if (pass == 0) count += total;
         __syncthreads();
       }
       if (pass == 0) {
-        int all;
-        const int off = block_exclusive_scan(t < NBK ? hist[t] : 0, s_tmp, &all);
-        if (t < NBK) hist[t] = off;
+        // bucket offsets: wavefront 0 scans the tiles', wavefront 1 the units'
+        if (t < 64) wave_scan_256(hist);
+        else if (t < 128 && units != nullptr) {
+          const int all = wave_scan_256(uhist);
+          if (t == 64) s_tmp[16] = all;
+        }
         __syncthreads();
+        if (units != nullptr) nu = s_tmp[16];
       }
     }
     if (t == 0) *num_tiles = min(count, tile_cap);
+    if (t == 0 && units != nullptr) num_tiles[1] = min(nu, unit_cap);
   }
+  if (vctx == nullptr && vrow == nullptr) return;
   for (int tok = t; tok < num_tokens; tok += blockDim.x) {
     // the sequence that owns tok: the last b with query_start[b] <= tok
     int lo = 0, hi = num_seqs - 1;
@@ -279,7 +358,7 @@ __global__ __launch_bounds__(1024) void mq_plan_kernel(const int32_t* __restrict
     const int q0 = qstart(lo);
     const int n = qstart(lo + 1) - q0;
     const int pos = ctx(lo) - n + (tok - q0);
-    vctx[tok] = min(max(pos + 1, 0), max_context_len);
+    if (vctx != nullptr) vctx[tok] = min(max(pos + 1, 0), max_context_len);
     if (vrow != nullptr) vrow[tok] = lo;
   }
 }

@@ -288,6 +288,27 @@ def test_mq_mixed_batch(P, W):
     check(DeviceMQ(c).run(tiled=False), want, "bf16")
 
 
+@pytest.mark.parametrize("P,W", [(64, 0), (64, 100), (48, 20)])
+def test_mq_unit_list_matches_plan_order(P, W):
+    """With keys split, the shared kernel walks the plan's sorted (tile,
+    partition) list; each unit's results do not depend on when it runs, so
+    the output equals, bit for bit, that of the grid in plan order with
+    partitions slowest (PA_MQ_UNITS=0), and matches the oracle."""
+    from gpu_util import say, to_f64
+    say(f"mq unit list P={P} W={W}")
+    rng = np.random.default_rng(900 + P + W)
+    L = [700, 1, 300, 64, 0, 1200, 33, 500, 90, 257]
+    n = [96, 1, 1, 64, 0, 1, 5, 1, 40, 1]
+    c = make_mq_case(Hq=8, Hkv=4, D=256, bs=16, dtype="bf16", context_lens=L, query_lens=n,
+                     softcap=50.0, window=W, partition_size=P, seed=int(rng.integers(1 << 30)),
+                     new_rows=True)
+    dev = DeviceMQ(c)
+    by_units = to_f64(dev.run(shared=True))
+    in_order = to_f64(dev.run(shared=True, env={"PA_MQ_UNITS": "0"}))
+    assert np.array_equal(by_units, in_order)
+    check(dev.run(shared=True), oracle.multi_query_case(c), "bf16")
+
+
 @pytest.mark.parametrize("B", [400, 700])
 @pytest.mark.parametrize("path", ["wave", "wave-split"])
 def test_mq_resident_order(B, path):
