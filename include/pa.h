@@ -262,6 +262,56 @@ int pa_mq_attention(void* out, void* workspace, size_t workspace_bytes, const vo
                     pa_dtype dtype, void* stream);
 
 /*
+ * One multi-query layer-step: the new tokens' K and V are appended to the
+ * cache and the new tokens attend (ovshake/nano-vllm README, "Key Concepts
+ * Explained: KV Cache": a step computes K and V for its new tokens only and
+ * adds them to what is cached; "Features", "Advanced Scheduling" for prompt
+ * chunks beside decoding sequences).  Results equal, bit for bit,
+ * pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping,
+ * num_new_rows, ...) followed by pa_mq_attention(...) with the other
+ * fields, on `stream`; one launch writes the rows and builds the plan (two
+ * launches in the two calls).  num_new_rows may differ from num_tokens
+ * (0: no rows).  Errors: those of the two calls, checked before anything is
+ * enqueued (where the attention arguments are wrong, the fused step writes
+ * no rows, which the two calls would have written first).  Environment
+ * PA_STEP_FUSE=0 makes it issue the two calls instead.
+ */
+typedef struct {
+  /* pa_reshape_and_cache (skipped when num_new_rows == 0) */
+  const void* key;
+  const void* value;
+  const int64_t* slot_mapping;
+  int num_new_rows;
+  /* pa_mq_attention */
+  void* out;
+  void* workspace;
+  size_t workspace_bytes;
+  const void* q;
+  const int32_t* query_start;
+  int num_tokens;
+  int max_query_len;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  const int32_t* context_lens;
+  int max_context_len;
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int head_dim;
+  int block_size;
+  int num_blocks;
+  float scale;
+  float softcap;
+  int window;
+  int partition_size;
+  pa_dtype dtype;
+} pa_mq_step_args;
+
+int pa_mq_step(const pa_mq_step_args* args, void* stream);
+
+/*
  * One layer-step: pa_reshape_and_cache (when num_tokens > 0), pa_decode and
  * pa_decode_reduce with the arguments below, on one stream.  The step can
  * also be captured once into a HIP graph and replayed: static graph execution

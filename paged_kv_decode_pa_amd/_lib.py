@@ -23,7 +23,7 @@ EXPORTS = ("pa_status_string", "pa_reshape_and_cache", "pa_decode_partition_size
            "pa_mq_partition_size", "pa_mq_workspace_size", "pa_mq_attention", "pa_step",
            "pa_step_graph_create", "pa_step_graph_create_n", "pa_step_graph_launch",
            "pa_step_graph_destroy", "pa_step_static", "pa_set_decode_events",
-           "pa_read_bandwidth_probe")
+           "pa_read_bandwidth_probe", "pa_mq_step")
 
 
 class StepArgs(ctypes.Structure):
@@ -43,6 +43,27 @@ class StepArgs(ctypes.Structure):
         ("partition_size", ctypes.c_int), ("dtype", ctypes.c_int),
         ("new_rows_at_tails", ctypes.c_int),
     ]
+
+
+class MQStepArgs(ctypes.Structure):
+    """pa_mq_step_args (include/pa.h)."""
+    _fields_ = [
+        ("key", ctypes.c_void_p), ("value", ctypes.c_void_p),
+        ("slot_mapping", ctypes.c_void_p), ("num_new_rows", ctypes.c_int),
+        ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t), ("q", ctypes.c_void_p),
+        ("query_start", ctypes.c_void_p), ("num_tokens", ctypes.c_int),
+        ("max_query_len", ctypes.c_int),
+        ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("block_tables", ctypes.c_void_p), ("max_blocks_per_seq", ctypes.c_int),
+        ("context_lens", ctypes.c_void_p), ("max_context_len", ctypes.c_int),
+        ("num_seqs", ctypes.c_int), ("num_heads", ctypes.c_int),
+        ("num_kv_heads", ctypes.c_int), ("head_dim", ctypes.c_int),
+        ("block_size", ctypes.c_int), ("num_blocks", ctypes.c_int),
+        ("scale", ctypes.c_float), ("softcap", ctypes.c_float), ("window", ctypes.c_int),
+        ("partition_size", ctypes.c_int), ("dtype", ctypes.c_int),
+    ]
+
 
 _lib = None
 
@@ -100,6 +121,8 @@ def load() -> ctypes.CDLL:
     lib.pa_step_static.argtypes = [sp, vp]
     lib.pa_set_decode_events.restype = i32
     lib.pa_set_decode_events.argtypes = [vp, vp]
+    lib.pa_mq_step.restype = i32
+    lib.pa_mq_step.argtypes = [ctypes.POINTER(MQStepArgs), vp]
     lib.pa_read_bandwidth_probe.restype = i32
     lib.pa_read_bandwidth_probe.argtypes = [vp, sz, i32, vp, vp]
     _lib = lib

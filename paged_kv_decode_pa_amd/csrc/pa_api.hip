@@ -683,13 +683,17 @@ size_t pa_mq_workspace_size(int num_seqs, int num_tokens, int num_heads, int num
                                   partition_size);
 }
 
-int pa_mq_attention(void* out, void* workspace, size_t workspace_bytes, const void* q,
-                    const int32_t* query_start, int num_tokens, int max_query_len,
-                    const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                    int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
-                    int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
-                    int num_blocks, float scale, float softcap, int window, int partition_size,
-                    pa_dtype dtype, void* stream) {
+// pa_mq_attention; with `rows`, its plan launch also writes the step's new
+// K/V rows (the caller has checked them).
+static int mq_attention_impl(void* out, void* workspace, size_t workspace_bytes, const void* q,
+                             const int32_t* query_start, int num_tokens, int max_query_len,
+                             const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, int max_blocks_per_seq,
+                             const int32_t* context_lens, int max_context_len, int num_seqs,
+                             int num_heads, int num_kv_heads, int head_dim, int block_size,
+                             int num_blocks, float scale, float softcap, int window,
+                             int partition_size, pa_dtype dtype, void* stream,
+                             const pa::NewRows* rows) {
   if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
       num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || window < 0 ||
       partition_size < 0)
@@ -748,13 +752,34 @@ int pa_mq_attention(void* out, void* workspace, size_t workspace_bytes, const vo
   const bool by_units = wg && np > 1 && env_int("PA_MQ_UNITS", 1) != 0;
   const bool split = partials_bytes(num_tokens, num_heads, head_dim, max_context_len,
                                     partition_size) != 0;
-  pa::mq_plan_kernel<<<dim3(1), dim3(1024), 0, s>>>(
-      query_start, context_lens, num_seqs, num_tokens, max_context_len, window, G, R,
-      tiled ? tiles : nullptr, (int)mq_max_tiles(num_seqs, num_tokens, G, R), num_tiles,
-      partition_size, by_units ? units : nullptr,
-      (int)mq_unit_cap(num_seqs, num_tokens, G, np),
-      // token contexts: the per-token path's sequences, or the reduce's rows
-      !tiled || split ? vctx : nullptr, tiled ? nullptr : vrow);
+  pa::MQPlanArgs pl{};
+  pl.query_start = query_start;
+  pl.context_lens = context_lens;
+  pl.num_seqs = num_seqs;
+  pl.num_tokens = num_tokens;
+  pl.max_context_len = max_context_len;
+  pl.window = window;
+  pl.G = G;
+  pl.R = R;
+  pl.tiles = tiled ? tiles : nullptr;
+  pl.tile_cap = (int)mq_max_tiles(num_seqs, num_tokens, G, R);
+  pl.num_tiles = num_tiles;
+  pl.part_size = partition_size;
+  pl.units = by_units ? units : nullptr;
+  pl.unit_cap = (int)mq_unit_cap(num_seqs, num_tokens, G, np);
+  // token contexts: the per-token path's sequences, or the reduce's rows
+  pl.vctx = !tiled || split ? vctx : nullptr;
+  pl.vrow = tiled ? nullptr : vrow;
+  if (rows != nullptr && rows->num_tokens > 0) {
+    // copy workgroups: one 16-byte piece of K and of V per thread and pass,
+    // at most two per CU
+    const long pieces = (long)rows->num_tokens * rows->row16;
+    const long need = (pieces + 1023) / 1024;
+    const long wgs = need < 2L * kNumCUs ? need : 2L * kNumCUs;
+    pa::mq_step_prep_kernel<<<dim3(1 + (unsigned)wgs), dim3(1024), 0, s>>>(pl, *rows);
+  }
+  else
+    pa::mq_plan_kernel<<<dim3(1), dim3(1024), 0, s>>>(pl);
   if (hipGetLastError() != hipSuccess) return PA_ELAUNCH;
 
   int rc;
@@ -871,6 +896,63 @@ int pa_mq_attention(void* out, void* workspace, size_t workspace_bytes, const vo
   // split-K partials of tokens whose keys span several partitions
   return pa_decode_reduce(out, dws, dws_bytes, vctx, max_context_len, num_tokens, num_heads,
                           head_dim, partition_size, window, dtype, stream);
+}
+
+int pa_mq_attention(void* out, void* workspace, size_t workspace_bytes, const void* q,
+                    const int32_t* query_start, int num_tokens, int max_query_len,
+                    const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                    int max_blocks_per_seq, const int32_t* context_lens, int max_context_len,
+                    int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                    int num_blocks, float scale, float softcap, int window, int partition_size,
+                    pa_dtype dtype, void* stream) {
+  return mq_attention_impl(out, workspace, workspace_bytes, q, query_start, num_tokens,
+                           max_query_len, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                           context_lens, max_context_len, num_seqs, num_heads, num_kv_heads,
+                           head_dim, block_size, num_blocks, scale, softcap, window,
+                           partition_size, dtype, stream, nullptr);
+}
+
+int pa_mq_step(const pa_mq_step_args* a, void* stream) {
+  if (!a) return PA_EINVAL;
+  const int T = a->num_new_rows;
+  if (T < 0) return PA_EINVAL;
+  if (T > 0) {  // the checks of pa_reshape_and_cache
+    if (a->num_blocks <= 0 || a->num_kv_heads <= 0) return PA_EINVAL;
+    if (!valid_dtype(a->dtype) || !supported_head_dim(a->head_dim) ||
+        !pow2_in(a->block_size, 1, 256))
+      return PA_EUNSUPPORTED;
+    if (!a->key || !a->value || !a->k_cache || !a->v_cache || !a->slot_mapping) return PA_EINVAL;
+  }
+  if (T == 0 || a->num_tokens <= 0 || env_int("PA_STEP_FUSE", 1) == 0) {
+    // the two entry points one after the other
+    if (T > 0) {
+      const int st = pa_reshape_and_cache(a->key, a->value, a->k_cache, a->v_cache,
+                                          a->slot_mapping, T, a->num_blocks, a->block_size,
+                                          a->num_kv_heads, a->head_dim, a->dtype, stream);
+      if (st != PA_OK) return st;
+    }
+    return pa_mq_attention(a->out, a->workspace, a->workspace_bytes, a->q, a->query_start,
+                           a->num_tokens, a->max_query_len, a->k_cache, a->v_cache,
+                           a->block_tables, a->max_blocks_per_seq, a->context_lens,
+                           a->max_context_len, a->num_seqs, a->num_heads, a->num_kv_heads,
+                           a->head_dim, a->block_size, a->num_blocks, a->scale, a->softcap,
+                           a->window, a->partition_size, a->dtype, stream);
+  }
+  pa::NewRows r{};
+  r.key = static_cast<const uint4*>(a->key);
+  r.value = static_cast<const uint4*>(a->value);
+  r.k_cache = static_cast<uint4*>(a->k_cache);
+  r.v_cache = static_cast<uint4*>(a->v_cache);
+  r.slot_mapping = a->slot_mapping;
+  r.num_tokens = T;
+  r.num_slots = (int64_t)a->num_blocks * a->block_size;
+  r.row16 = (int)((int64_t)a->num_kv_heads * a->head_dim * elem_bytes(a->dtype) / 16);
+  return mq_attention_impl(a->out, a->workspace, a->workspace_bytes, a->q, a->query_start,
+                           a->num_tokens, a->max_query_len, a->k_cache, a->v_cache,
+                           a->block_tables, a->max_blocks_per_seq, a->context_lens,
+                           a->max_context_len, a->num_seqs, a->num_heads, a->num_kv_heads,
+                           a->head_dim, a->block_size, a->num_blocks, a->scale, a->softcap,
+                           a->window, a->partition_size, a->dtype, stream, &r);
 }
 
 }  // extern "C"

@@ -174,25 +174,61 @@ struct PrepParams {
   int row16;
 };
 
+// Rows 4 wg .. 4 wg + 3 of a step's new K/V rows, 256 threads a row.
+__device__ __forceinline__ void copy_new_rows(const uint4* key, const uint4* value,
+                                              uint4* k_cache, uint4* v_cache,
+                                              const int64_t* slot_mapping, int num_tokens,
+                                              int64_t num_slots, int row16, int wg) {
+  const int i = wg * 4 + (int)(threadIdx.x >> 8);
+  if (i >= num_tokens) return;
+  const int64_t s = slot_mapping[i];
+  if (s < 0 || s >= num_slots) return;
+  const uint4* ks = key + (int64_t)i * row16;
+  const uint4* vs = value + (int64_t)i * row16;
+  uint4* kd = k_cache + s * row16;
+  uint4* vd = v_cache + s * row16;
+  for (int j = threadIdx.x & 255; j < row16; j += 256) {
+    kd[j] = ks[j];
+    vd[j] = vs[j];
+  }
+}
+
 __global__ __launch_bounds__(1024) void step_prep_kernel(PrepParams pp) {
   if (blockIdx.x == 0) {
     if (pp.plan.order != nullptr)
       plan_body(pp.context_lens, pp.num_seqs, pp.max_context_len, pp.window, pp.part, pp.plan);
     return;
   }
-  const int i = (int)(blockIdx.x - 1) * 4 + (int)(threadIdx.x >> 8);
-  if (i >= pp.num_tokens) return;
-  const int64_t s = pp.slot_mapping[i];
-  if (s < 0 || s >= pp.num_slots) return;
-  const uint4* ks = pp.key + (int64_t)i * pp.row16;
-  const uint4* vs = pp.value + (int64_t)i * pp.row16;
-  uint4* kd = pp.k_cache + s * pp.row16;
-  uint4* vd = pp.v_cache + s * pp.row16;
-  for (int j = threadIdx.x & 255; j < pp.row16; j += 256) {
-    kd[j] = ks[j];
-    vd[j] = vs[j];
-  }
+  copy_new_rows(pp.key, pp.value, pp.k_cache, pp.v_cache, pp.slot_mapping, pp.num_tokens,
+                pp.num_slots, pp.row16, (int)blockIdx.x - 1);
 }
+
+// A multi-query step's new K/V rows (the copy of reshape_cache_kernel).
+struct NewRows {
+  const uint4* key;      // [num_tokens, row16]
+  const uint4* value;
+  uint4* k_cache;        // [num_slots, row16]
+  uint4* v_cache;
+  const int64_t* slot_mapping;
+  int num_tokens;
+  int64_t num_slots;
+  int row16;
+};
+
+// Arguments of the multi-query plan (described below).
+struct MQPlanArgs {
+  const int32_t* query_start;
+  const int32_t* context_lens;
+  int num_seqs, num_tokens, max_context_len, window, G, R;
+  int2* tiles;
+  int tile_cap;
+  int32_t* num_tiles;
+  int part_size;
+  int2* units;
+  int unit_cap;
+  int32_t* vctx;
+  int32_t* vrow;
+};
 
 // Plan of a multi-query launch (one workgroup of 1024 threads):
 //   vctx[tok] = context of query token tok (its position + 1, clamped to
@@ -215,14 +251,19 @@ __global__ __launch_bounds__(1024) void step_prep_kernel(PrepParams pp) {
 //   CUs in turn, so each run of 256 workgroups puts one on every CU and the
 //   heaviest units spread evenly.
 //   Null outputs are skipped (vctx and vrow together skip the token loop).
-__global__ __launch_bounds__(1024) void mq_plan_kernel(const int32_t* __restrict__ query_start,
-                                                       const int32_t* __restrict__ context_lens,
-                                                       int num_seqs, int num_tokens,
-                                                       int max_context_len, int window, int G,
-                                                       int R, int2* tiles, int tile_cap,
-                                                       int32_t* num_tiles, int part_size,
-                                                       int2* units, int unit_cap,
-                                                       int32_t* vctx, int32_t* vrow) {
+__device__ __forceinline__ void mq_plan_body(const MQPlanArgs& a) {
+  const int32_t* __restrict__ query_start = a.query_start;
+  const int32_t* __restrict__ context_lens = a.context_lens;
+  const int num_seqs = a.num_seqs, num_tokens = a.num_tokens;
+  const int max_context_len = a.max_context_len, window = a.window, G = a.G, R = a.R;
+  int2* tiles = a.tiles;
+  const int tile_cap = a.tile_cap;
+  int32_t* num_tiles = a.num_tiles;
+  const int part_size = a.part_size;
+  int2* units = a.units;
+  const int unit_cap = a.unit_cap;
+  int32_t* vctx = a.vctx;
+  int32_t* vrow = a.vrow;
   constexpr int kQS = 4096;  // sequence starts and contexts kept in LDS up to this many
   constexpr int NBK = 256;
   __shared__ int s_tmp[17];
@@ -360,6 +401,29 @@ __global__ __launch_bounds__(1024) void mq_plan_kernel(const int32_t* __restrict
     const int pos = ctx(lo) - n + (tok - q0);
     if (vctx != nullptr) vctx[tok] = min(max(pos + 1, 0), max_context_len);
     if (vrow != nullptr) vrow[tok] = lo;
+  }
+}
+
+__global__ __launch_bounds__(1024) void mq_plan_kernel(MQPlanArgs a) { mq_plan_body(a); }
+
+// A multi-query step's one launch before the attention: workgroup 0 builds
+// the plan, workgroups 1.. copy the new K/V rows, every thread moving 16
+// bytes of K and of V per step over all rows' 16-byte pieces (a prompt's
+// rows can be short and many: 8,192 of 512 bytes).
+__global__ __launch_bounds__(1024) void mq_step_prep_kernel(MQPlanArgs a, NewRows r) {
+  if (blockIdx.x == 0) {
+    mq_plan_body(a);
+    return;
+  }
+  const int64_t n = (int64_t)r.num_tokens * r.row16;
+  const int64_t stride = (int64_t)(gridDim.x - 1) * blockDim.x;
+  for (int64_t e = (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x; e < n; e += stride) {
+    const int i = (int)(e / r.row16);
+    const int j = (int)(e - (int64_t)i * r.row16);
+    const int64_t s = r.slot_mapping[i];
+    if (s < 0 || s >= r.num_slots) continue;
+    r.k_cache[s * r.row16 + j] = r.key[e];
+    r.v_cache[s * r.row16 + j] = r.value[e];
   }
 }
 

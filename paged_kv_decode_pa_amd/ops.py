@@ -201,7 +201,7 @@ def mq_workspace_size(num_seqs, num_tokens, num_heads, num_kv_heads, head_dim, m
 
 def mq_attention(q, query_start, k_cache, v_cache, block_tables, context_lens, scale, softcap=0.0,
                  window=0, partition_size=None, max_context_len=None, max_query_len=None,
-                 out=None, workspace=None):
+                 out=None, workspace=None, key=None, value=None, slot_mapping=None):
     """Multi-query paged attention (pa_mq_attention): sequence b's new tokens
     are q's rows query_start[b] .. query_start[b+1]-1, the last n_b of its
     context_lens[b] positions, each attending causally to the keys up to its
@@ -210,8 +210,12 @@ def mq_attention(q, query_start, k_cache, v_cache, block_tables, context_lens, s
     q [T, Hq, D]; query_start int32 [B+1]; context_lens int32 [B] (counting
     the new tokens, whose K/V rows are already in the cache).
     ``max_context_len`` / ``max_query_len`` default to the maxima of the
-    device arrays (one device sync each)."""
-    _dev(q, query_start, k_cache, v_cache, block_tables, context_lens, out)
+    device arrays (one device sync each).
+    With ``key``/``value`` ([N, Hkv, D]) and ``slot_mapping`` (int64 [N]),
+    the call first writes those rows into the caches as reshape_and_cache
+    does, in the same launch as the plan (pa_mq_step)."""
+    _dev(q, query_start, k_cache, v_cache, block_tables, context_lens, out, key, value,
+         slot_mapping)
     T, Hq, D = q.shape
     NB, bs, Hkv, D2 = k_cache.shape
     B = context_lens.shape[0]
@@ -242,12 +246,97 @@ def mq_attention(q, query_start, k_cache, v_cache, block_tables, context_lens, s
         workspace = torch.empty((n + 3) // 4, dtype=torch.float32, device=q.device) if n else None
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if slot_mapping is not None:
+        a = _mq_step_args(q, query_start, k_cache, v_cache, block_tables, context_lens, scale,
+                          softcap, window, partition_size, max_context_len, max_query_len, out,
+                          workspace, key, value, slot_mapping)
+        _lib.check("pa_mq_step", _lib.load().pa_mq_step(ctypes.byref(a), _stream()))
+        return out
+    if key is not None or value is not None:
+        raise ValueError("key/value need slot_mapping")
     _lib.check("pa_mq_attention", _lib.load().pa_mq_attention(
         out.data_ptr(), ws_ptr, ws_bytes, q.data_ptr(), query_start.data_ptr(), T,
         int(max_query_len), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
         block_tables.shape[1], context_lens.data_ptr(), int(max_context_len), B, Hq, Hkv, D, bs,
         NB, float(scale), float(softcap), int(window), int(partition_size), _dt(q), _stream()))
     return out
+
+
+def _mq_step_args(q, query_start, k_cache, v_cache, block_tables, context_lens, scale, softcap,
+                  window, partition_size, max_context_len, max_query_len, out, workspace, key,
+                  value, slot_mapping):
+    """pa_mq_step_args for checked tensors (sizes as mq_attention resolved them)."""
+    T, Hq, D = q.shape
+    NB, bs, Hkv, _ = k_cache.shape
+    B = context_lens.shape[0]
+    if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1:
+        raise TypeError("slot_mapping must be int64 [N]")
+    N = slot_mapping.shape[0]
+    if key is None or value is None or tuple(key.shape) != (N, Hkv, D) \
+            or tuple(value.shape) != (N, Hkv, D):
+        raise ValueError("key/value must be [N, Hkv, D] beside slot_mapping [N]")
+    if not (key.dtype == value.dtype == q.dtype):
+        raise TypeError("key, value and caches must share a dtype")
+    a = _lib.MQStepArgs()
+    a.key, a.value, a.slot_mapping = key.data_ptr(), value.data_ptr(), slot_mapping.data_ptr()
+    a.num_new_rows = N
+    a.out, a.q = out.data_ptr(), q.data_ptr()
+    a.workspace = workspace.data_ptr() if workspace is not None else None
+    a.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    a.query_start, a.num_tokens, a.max_query_len = query_start.data_ptr(), T, int(max_query_len)
+    a.k_cache, a.v_cache = k_cache.data_ptr(), v_cache.data_ptr()
+    a.block_tables, a.max_blocks_per_seq = block_tables.data_ptr(), block_tables.shape[1]
+    a.context_lens, a.max_context_len = context_lens.data_ptr(), int(max_context_len)
+    a.num_seqs, a.num_heads, a.num_kv_heads, a.head_dim = B, Hq, Hkv, D
+    a.block_size, a.num_blocks = bs, NB
+    a.scale, a.softcap, a.window = float(scale), float(softcap), int(window)
+    a.partition_size, a.dtype = int(partition_size), _dt(q)
+    return a
+
+
+class MQStep:
+    """One multi-query layer-step over fixed buffers (pa_mq_step): the new
+    K/V rows written into their slots and the new tokens' attention, built
+    once (sizes resolved, output and workspace allocated) and enqueued by
+    ``run`` with one native call.  Buffer contents may change between runs;
+    the tensors and the host-side sizes are fixed at construction."""
+
+    def __init__(self, q, query_start, k_cache, v_cache, block_tables, context_lens, scale,
+                 softcap=0.0, window=0, partition_size=None, max_context_len=None,
+                 max_query_len=None, out=None, key=None, value=None, slot_mapping=None):
+        _dev(q, query_start, k_cache, v_cache, block_tables, context_lens, out, key, value,
+             slot_mapping)
+        T, Hq, D = q.shape
+        NB, bs, Hkv, _ = k_cache.shape
+        B = context_lens.shape[0]
+        if max_context_len is None:
+            max_context_len = int(context_lens.max().item()) if B else 0
+        if max_query_len is None:
+            max_query_len = int((query_start[1:] - query_start[:-1]).max().item()) if B else 0
+        max_query_len = max(1, min(int(max_query_len), T)) if T else 0
+        if partition_size is None:
+            partition_size = mq_partition_size(B, T, max(max_query_len, 1), Hq, Hkv, D, bs,
+                                               max_context_len, window, q.dtype)
+        self.out = torch.empty_like(q) if out is None else out
+        n = mq_workspace_size(B, T, Hq, Hkv, D, max_context_len, partition_size)
+        self.workspace = (torch.empty((n + 3) // 4, dtype=torch.float32, device=q.device)
+                          if n else None)
+        if slot_mapping is None:  # no new rows
+            slot_mapping = torch.empty(0, dtype=torch.int64, device=q.device)
+            key = value = torch.empty((0, Hkv, D), dtype=q.dtype, device=q.device)
+        self.args = _mq_step_args(q, query_start, k_cache, v_cache, block_tables, context_lens,
+                                  scale, softcap, window, partition_size, max_context_len,
+                                  max_query_len, self.out, self.workspace, key, value,
+                                  slot_mapping)
+        self.partition_size = int(partition_size)
+        # keep every buffer alive as long as the step exists
+        self._keep = (q, query_start, k_cache, v_cache, block_tables, context_lens, key, value,
+                      slot_mapping, self.out, self.workspace)
+
+    def run(self):
+        """Enqueue the step on torch's current stream."""
+        _lib.check("pa_mq_step", _lib.load().pa_mq_step(ctypes.byref(self.args), _stream()))
+        return self.out
 
 
 class Step:

@@ -148,20 +148,22 @@ def test_binding_refuses_host_tensors():
                   0.125, max_context_len=1, partition_size=0)
 
 
-def test_step_args_layout_matches_the_header(tmp_path):
-    """The ctypes mirror of pa_step_args has the C struct's size and offsets
-    (checked with the host C compiler)."""
+@pytest.mark.parametrize("mirror,cname", [(_lib.StepArgs, "pa_step_args"),
+                                          (_lib.MQStepArgs, "pa_mq_step_args")])
+def test_step_args_layout_matches_the_header(tmp_path, mirror, cname):
+    """The ctypes mirrors of pa_step_args and pa_mq_step_args have the C
+    structs' sizes and offsets (checked with the host C compiler)."""
     import shutil
     import subprocess
     cc = shutil.which("gcc") or shutil.which("cc")
     if cc is None:
         pytest.skip("no host C compiler")
-    fields = [f for f, _ in _lib.StepArgs._fields_]
+    fields = [f for f, _ in mirror._fields_]
     src = tmp_path / "layout.c"
     src.write_text(
         "#include <stdio.h>\n#include <stddef.h>\n#include \"pa.h\"\n"
-        "int main(void) { printf(\"%zu\\n\", sizeof(pa_step_args));\n"
-        + "".join(f'  printf("%zu\\n", offsetof(pa_step_args, {f}));\n' for f in fields)
+        f"int main(void) {{ printf(\"%zu\\n\", sizeof({cname}));\n"
+        + "".join(f'  printf("%zu\\n", offsetof({cname}, {f}));\n' for f in fields)
         + "  return 0; }\n")
     exe = tmp_path / "layout"
     # pa.h only needs the standard headers for this; hipStream_t is void*
@@ -169,9 +171,9 @@ def test_step_args_layout_matches_the_header(tmp_path):
                    check=True)
     got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
                                           check=True).stdout.split()]
-    assert got[0] == ctypes.sizeof(_lib.StepArgs)
+    assert got[0] == ctypes.sizeof(mirror)
     for f, off in zip(fields, got[1:]):
-        assert getattr(_lib.StepArgs, f).offset == off, f
+        assert getattr(mirror, f).offset == off, f
 
 
 def test_step_graph_argument_checks():
@@ -221,6 +223,42 @@ def call_mq(a):
 ])
 def test_mq_rejects_bad_arguments(over, status):
     assert call_mq(mq_args(**over)) == status
+
+
+def mq_step_args(rows=3, **over):
+    a = mq_args(**over)
+    s = _lib.MQStepArgs()
+    s.key, s.value, s.slot_mapping, s.num_new_rows = FAKE, FAKE, FAKE, rows
+    s.out, s.workspace, s.workspace_bytes, s.q = a["out"], a["ws"], a["ws_bytes"], a["q"]
+    s.query_start, s.num_tokens, s.max_query_len = a["qs"], a["T"], a["maxq"]
+    s.k_cache, s.v_cache, s.block_tables, s.max_blocks_per_seq = a["kc"], a["vc"], a["bt"], a["maxb"]
+    s.context_lens, s.max_context_len, s.num_seqs = a["cl"], a["maxL"], a["B"]
+    s.num_heads, s.num_kv_heads, s.head_dim, s.block_size = a["Hq"], a["Hkv"], a["D"], a["bs"]
+    s.num_blocks, s.scale, s.softcap, s.window = a["NB"], a["scale"], a["softcap"], a["window"]
+    s.partition_size, s.dtype = a["P"], a["dt"]
+    return s
+
+
+@pytest.mark.parametrize("rows,over,fields,status", [
+    (-1, {}, {}, -1),
+    (3, {}, dict(key=None), -1),
+    (3, {}, dict(slot_mapping=None), -1),
+    (3, dict(NB=0), {}, -1),
+    (3, dict(bs=24), {}, -2),
+    (3, dict(D=80), {}, -2),
+    (3, dict(out=None), {}, -1),          # attention errors, checked before the fused launch
+    (3, dict(maxq=13), {}, -1),
+    (3, {}, {}, -3),                      # no workspace
+    (0, {}, {}, -3),                      # no rows: pa_mq_attention alone
+])
+def test_mq_step_rejects_bad_arguments(rows, over, fields, status):
+    """pa_mq_step reports the errors of pa_reshape_and_cache and
+    pa_mq_attention before anything is enqueued."""
+    a = mq_step_args(rows, **over)
+    for k, v in fields.items():
+        setattr(a, k, v)
+    assert _lib.load().pa_mq_step(ctypes.byref(a), None) == status
+    assert _lib.load().pa_mq_step(None, None) == -1
 
 
 def test_mq_with_no_tokens_is_a_noop():

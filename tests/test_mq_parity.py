@@ -309,6 +309,67 @@ def test_mq_unit_list_matches_plan_order(P, W):
     check(dev.run(shared=True), oracle.multi_query_case(c), "bf16")
 
 
+def _bits(t):
+    import torch
+    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("P,W,tiled", [(64, 100, True), (0, 0, True), (32, 0, False)])
+def test_mq_step_matches_reshape_then_attention(P, W, tiled):
+    """pa_mq_step, whose plan launch also writes the new K/V rows, leaves the
+    caches and the output bit for bit as reshape_and_cache followed by
+    pa_mq_attention do; two extra rows with slot -1 and a slot past the pool
+    are skipped by both.  The output also matches the oracle."""
+    import torch
+    import paged_kv_decode_pa_amd as pa
+    from gpu_util import say
+    say(f"mq step P={P} W={W} tiled={tiled}")
+    rng = np.random.default_rng(1200 + P + W)
+    L = [700, 1, 300, 64, 0, 1200, 33, 500, 90, 257]
+    n = [96, 1, 1, 64, 0, 1, 5, 1, 40, 1]
+    dt = "bf16" if tiled else "f16"
+    c = make_mq_case(Hq=8, Hkv=4, D=128, bs=16, dtype=dt, context_lens=L, query_lens=n,
+                     softcap=30.0, window=W, partition_size=P, seed=int(rng.integers(1 << 30)),
+                     new_rows=True)
+    dev = DeviceMQ(c)
+    NB, bs = c.k_cache.shape[:2]
+    key = torch.cat([dev.key, dev.key[:2]])
+    value = torch.cat([dev.value, dev.value[:2]])
+    slots = torch.cat([dev.slots, torch.tensor([-1, NB * bs + 3], dtype=torch.int64,
+                                               device=dev.slots.device)])
+    kc0, vc0 = dev.k_cache.clone(), dev.v_cache.clone()
+    args = (dev.q, dev.query_start, dev.k_cache, dev.v_cache, dev.block_tables,
+            dev.context_lens, c.scale, c.softcap, c.window)
+    kw = dict(partition_size=P, max_context_len=c.max_context_len,
+              max_query_len=max(1, c.max_query_len))
+    os.environ["PA_MQ_TILED"] = "1" if tiled else "0"
+    try:
+        pa.reshape_and_cache(key, value, dev.k_cache, dev.v_cache, slots)
+        out_a = pa.mq_attention(*args, **kw)
+        torch.cuda.synchronize()
+        kc_a, vc_a = dev.k_cache.clone(), dev.v_cache.clone()
+        dev.k_cache.copy_(kc0)
+        dev.v_cache.copy_(vc0)
+        out_b = pa.mq_attention(*args, key=key, value=value, slot_mapping=slots, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(dev.k_cache), _bits(kc_a))
+        assert torch.equal(_bits(dev.v_cache), _bits(vc_a))
+        # the prebuilt step object, run twice on the original caches
+        dev.k_cache.copy_(kc0)
+        dev.v_cache.copy_(vc0)
+        st = pa.MQStep(*args, key=key, value=value, slot_mapping=slots, **kw)
+        st.run()
+        out_c = st.run().clone()
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("PA_MQ_TILED", None)
+    assert torch.equal(_bits(dev.k_cache), _bits(kc_a))
+    assert torch.equal(_bits(dev.v_cache), _bits(vc_a))
+    assert torch.equal(_bits(out_b), _bits(out_a))
+    assert torch.equal(_bits(out_c), _bits(out_a))
+    check(out_b, oracle.multi_query_case(c), dt)
+
+
 @pytest.mark.parametrize("B", [400, 700])
 @pytest.mark.parametrize("path", ["wave", "wave-split"])
 def test_mq_resident_order(B, path):
