@@ -441,6 +441,13 @@ __global__ __launch_bounds__(64 * kMaxWaves, PA_DECODE_MIN_WAVES) void decode_ke
   // position: row r's position c_tail * NT + r is clamped into [lo, L - 1]
   const int c_tail = tail ? (u.L - 1) / NT : -1;
   auto reads_tail = [&](int i) { return max(c_tail * NT + i * RPI + rsub, lo) >= u.L - 1; };
+  // The tail row's loads were issued after the first chunk's: wait for
+  // them here, once.  Left pending into the loop, they made the compiler's
+  // wait before each chunk's q.k count from them, i.e. wait for every load
+  // in flight, V of the chunk included, so that each chunk paid V's whole
+  // round trip; the first chunk's K and V were issued together, so this
+  // costs little.
+  if constexpr (TAIL) __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
 
 #pragma clang loop unroll(disable)
   for (; c <= c1; c += nw) {
