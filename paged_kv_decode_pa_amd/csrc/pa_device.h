@@ -114,6 +114,35 @@ __device__ __forceinline__ float dot16<DT_F32>(const uint4& k, const uint4& q, f
   return acc;
 }
 
+// two floats -> two packed 16-bit values (round to nearest even)
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (DT == DT_F16)
+    return __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)lo, (_Float16)hi});
+  else
+    return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)lo, (__bf16)hi});
+}
+
+// acc + a.lo * b.lo + a.hi * b.hi over two packed 16-bit values
+template <int DT>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+  if constexpr (DT == DT_F16)
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
+                                  acc, false);
+  else
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// x rounded to the storage type (round to nearest even), as float32;
+// float32 storage: x itself
+template <int DT>
+__device__ __forceinline__ float round_to(float x) {
+  if constexpr (DT == DT_F16) return (float)(_Float16)x;
+  else if constexpr (DT == DT_BF16) return (float)(__bf16)x;
+  else return x;
+}
+
 // Widen a 16-byte fragment to float32 (exact for every storage type).
 template <int DT>
 __device__ __forceinline__ void widen16(const uint4& v, float* o);

@@ -521,7 +521,9 @@ __global__ __launch_bounds__(64 * kMaxWaves, PA_DECODE_MIN_WAVES) void decode_ke
 #pragma unroll
     for (int k = 0; k < SPL; ++k) {
       const int idx = lane + 64 * k;
-      const float pk = fast_exp2(sv[k] - m_new);
+      // 16-bit storage: the probability as P.V uses it (rounded to the
+      // storage type), so the sum and the products see the same value
+      const float pk = round_to<DT>(fast_exp2(sv[k] - m_new));
       psum += pk;
       if (idx < SLOTS) sc[idx] = pk;
     }
@@ -544,17 +546,45 @@ __global__ __launch_bounds__(64 * kMaxWaves, PA_DECODE_MIN_WAVES) void decode_ke
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[h][e] *= a;
     }
+    if constexpr (DT == DT_F32) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float pr[G];
+      for (int i = 0; i < NI; ++i) {
+        float pr[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) pr[h] = sc[(i * RPI + rsub) * G + h];
-      float ve[EPL];
-      widen16<DT>(vr[i], ve);
+        for (int h = 0; h < G; ++h) pr[h] = sc[(i * RPI + rsub) * G + h];
+        float ve[EPL];
+        widen16<DT>(vr[i], ve);
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+        for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pr[h], ve[e], acc[h][e]);
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pr[h], ve[e], acc[h][e]);
+      }
+    } else {
+      // 16-bit storage: loads i and i + 1 hold the lane's dims of two
+      // tokens; element e of both goes into one packed pair (a byte
+      // permute), and one packed dot with the two tokens' probabilities
+      // adds both products (exact in float32) to acc[h][e]: half the
+      // instructions of widening each value and multiplying it per head.
+#pragma unroll
+      for (int i = 0; i < NI; i += 2) {
+        uint32_t pp[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          pp[h] = pack2<DT>(sc[(i * RPI + rsub) * G + h], sc[((i + 1) * RPI + rsub) * G + h]);
+        const uint32_t va[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+        const uint32_t vb[4] = {vr[i + 1].x, vr[i + 1].y, vr[i + 1].z, vr[i + 1].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          // (token i, token i + 1) of elements 2k and 2k + 1
+          const uint32_t lo = __builtin_amdgcn_perm(vb[k], va[k], 0x05040100u);
+          const uint32_t hi = __builtin_amdgcn_perm(vb[k], va[k], 0x07060302u);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            acc[h][2 * k] = dot2<DT>(lo, pp[h], acc[h][2 * k]);
+            acc[h][2 * k + 1] = dot2<DT>(hi, pp[h], acc[h][2 * k + 1]);
+          }
+        }
+      }
     }
     // the next chunk's V goes in flight
     __builtin_amdgcn_sched_barrier(0);

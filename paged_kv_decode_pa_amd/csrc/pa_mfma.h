@@ -54,14 +54,6 @@ __device__ __forceinline__ f32x4_t mfma_k16(const uint2& a, const uint2& b, f32x
                                                      __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
 }
 
-// two floats -> two packed 16-bit values (round to nearest even)
-template <int DT>
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  if constexpr (DT == DT_F16)
-    return __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)lo, (_Float16)hi});
-  else
-    return __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)lo, (__bf16)hi});
-}
 
 
 // Chunks in flight per wavefront.  Measured on the long-context workload:
