@@ -850,8 +850,14 @@ static int mq_attention_impl(void* out, void* workspace, size_t workspace_bytes,
     };
     bool ok;
     if (wg) {
-      const int tiles_per_chunk = block_size >= 32 && head_dim <= 128 ? 2 : 1;
       const int nbuf = env_int("PA_MQ_NBUF", 3);
+      // head_dim 64 over 32-token pages: 64-key chunks (two pages, four
+      // tiles) per workgroup step (PA_MQ_TILES=2 keeps one page a chunk)
+      const int tiles_per_chunk =
+          head_dim == 64 && block_size == 32 && nbuf == 3 && nr <= 2 &&
+                  env_int("PA_MQ_TILES", 4) == 4
+              ? 4
+              : (block_size >= 32 && head_dim <= 128 ? 2 : 1);
       ok = dtype == PA_F16
                ? pa::launch_mq_wg_f16(head_dim, nr, tiles_per_chunk, nbuf, grid, s, p)
                : pa::launch_mq_wg_bf16(head_dim, nr, tiles_per_chunk, nbuf, grid, s, p);

@@ -150,14 +150,15 @@ bool launch_mq_wg_bf16(int D, int nr, int tiles, int nbuf, dim3 grid, hipStream_
   }
 
 #define PA_MQ_WG_CASE(DT, DV, NRV, TV, BV)                                          \
-  case ((DV * 8 + NRV) * 4 + TV) * 8 + BV:                                          \
+  case ((DV * 8 + NRV) * 8 + TV) * 8 + BV:                                          \
     mq_wg_kernel<DT, DV, NRV, TV, BV><<<grid, dim3(256), 0, s>>>(p); /* static LDS */ \
     return true;
 
 #define PA_DEFINE_MQ_WG_LAUNCHER(NAME, DT)                                          \
   bool NAME(int D, int nr, int tiles, int nbuf, dim3 grid, hipStream_t s, const MQParams& p) { \
-    switch (((D * 8 + nr) * 4 + tiles) * 8 + nbuf) {                               \
+    switch (((D * 8 + nr) * 8 + tiles) * 8 + nbuf) {                               \
       PA_MQ_WG_CASE(DT, 64, 1, 1, 3) PA_MQ_WG_CASE(DT, 64, 1, 2, 3)                 \
+      PA_MQ_WG_CASE(DT, 64, 1, 4, 3) PA_MQ_WG_CASE(DT, 64, 2, 4, 3)                 \
       PA_MQ_WG_CASE(DT, 64, 2, 1, 3) PA_MQ_WG_CASE(DT, 64, 2, 2, 3)                 \
       PA_MQ_WG_CASE(DT, 64, 4, 1, 3) PA_MQ_WG_CASE(DT, 64, 4, 2, 3)                 \
       PA_MQ_WG_CASE(DT, 64, 2, 2, 4) PA_MQ_WG_CASE(DT, 64, 4, 2, 4)                 \

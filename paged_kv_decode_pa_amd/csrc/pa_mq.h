@@ -704,6 +704,11 @@ __global__ __launch_bounds__(256, (mq_wg_min_blocks<D, NR, TILES, NBUF_>())) voi
   // first LOADS are K, the rest V.  Lane l's 16 bytes land at byte
   // 1024 (q % LOADS) + 16 l of the K or V chunk: row r, stored segment
   // sg, global segment sg ^ swizzle(r).
+  // Four 16-token tiles a chunk (64 keys) span two 32-token pages: a
+  // wavefront's LPW = LOADS / 2 loads then cover one 32-row half of K
+  // (wavefronts 0, 1) or V (2, 3), addressed from that half's own page.
+  constexpr bool kTwoPages = TILES == 4;
+  static_assert(!kTwoPages || LPW * 2 == LOADS, "a wavefront's loads cover one half chunk");
   uint32_t ld_off[LPW];
 #pragma unroll
   for (int k = 0; k < LPW; ++k) {
@@ -711,7 +716,8 @@ __global__ __launch_bounds__(256, (mq_wg_min_blocks<D, NR, TILES, NBUF_>())) voi
     const int o = (q % LOADS) * 1024 + lane * 16;
     const int r = o / (2 * D);
     const int sg = (o % (2 * D)) >> 4;
-    ld_off[k] = (uint32_t)r * row_bytes + head_bytes +
+    const int r_src = kTwoPages ? r % (NT / 2) : r;  // row in the half's page
+    ld_off[k] = (uint32_t)r_src * row_bytes + head_bytes +
                 (uint32_t)((sg ^ (q < LOADS ? k_swz<D>(r) : v_swz<D>(r))) * 16);
   }
   // The copies of chunk c: the descriptors start at the chunk's first row
@@ -720,6 +726,32 @@ __global__ __launch_bounds__(256, (mq_wg_min_blocks<D, NR, TILES, NBUF_>())) voi
   // and their V rows then add nothing.  Rows before the first key (lo) are
   // earlier positions of the sequence, finite, and masked too.
   auto issue = [&](int c, char* kb) {
+    if constexpr (kTwoPages) {
+      // this wavefront's half: rows [cs, cs + NT / 2) of one page (the
+      // launch takes four tiles a chunk only over 32-token pages); a half
+      // with no key in [lo, hi) reads as zeros, as rows past hi do
+      const int cs = c * NT + (w & 1) * (NT / 2);
+      rsrc_t r = make_rsrc(dummy, 0u);
+      if (cs < hi && cs + NT / 2 > lo) {
+        const int cpg = cs >> log2_bs;
+        if (cpg < pg0 || cpg - pg0 >= 64) {
+          pg0 = cpg;
+          const int pg = cpg + lane;
+          tbl_v = pg <= last_pg ? bt[pg] : 0;
+          __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+        }
+        int phys = __builtin_amdgcn_readlane(tbl_v, cpg - pg0);
+        phys = ((unsigned)phys < (unsigned)p.num_blocks) ? phys : 0;
+        r = make_rsrc((w < 2 ? kbase : vbase) + (uint64_t)phys * page_bytes,
+                      (uint32_t)min(hi - cs, NT / 2) * row_bytes);
+      }
+#pragma unroll
+      for (int k = 0; k < LPW; ++k) {
+        const int q = LPW * w + k;
+        ld16_buf_to_lds(r, kb + (q < LOADS ? 0 : CBYTES) + (q % LOADS) * 1024, ld_off[k], 0);
+      }
+      return;
+    }
     rsrc_t kr, vr;
     if (c * NT < hi) {
       const int cs = c * NT;
@@ -904,13 +936,19 @@ __global__ __launch_bounds__(256, (mq_wg_min_blocks<D, NR, TILES, NBUF_>())) voi
       vt_frag<D, TILES>(vb, mt, c16, j, vv);
 #pragma unroll
       for (int nb = 0; nb < NR; ++nb) {
-        if constexpr (TILES == 2)
-          acc[nb][mt] = mfma_k32<DT>(make_uint4(vv[0], vv[1], vv[2], vv[3]),
-                                     make_uint4(pk[nb][0], pk[nb][1], pk[nb][2], pk[nb][3]),
-                                     acc[nb][mt]);
-        else
+        if constexpr (TILES == 1) {
           acc[nb][mt] = mfma_k16<DT>(make_uint2(vv[0], vv[1]), make_uint2(pk[nb][0], pk[nb][1]),
                                      acc[nb][mt]);
+        } else {
+          // 32 keys (two tiles) per 16x16x32 product
+#pragma unroll
+          for (int tp = 0; tp < TILES / 2; ++tp)
+            acc[nb][mt] = mfma_k32<DT>(
+                make_uint4(vv[4 * tp], vv[4 * tp + 1], vv[4 * tp + 2], vv[4 * tp + 3]),
+                make_uint4(pk[nb][4 * tp], pk[nb][4 * tp + 1], pk[nb][4 * tp + 2],
+                           pk[nb][4 * tp + 3]),
+                acc[nb][mt]);
+        }
       }
     }
   };

@@ -90,6 +90,10 @@ SHAPES = [
     ("bf16", 16, 64, 16, 20.0, 0, 0, [90, 31, 46], [3, 31, 5]),
     ("bf16", 3, 64, 16, 0.0, 0, 32, [70, 48], [11, 48]),     # group of 3 heads
     ("f16", 2, 64, 16, 0.0, 7, 16, [61, 18, 9], [13, 18, 9]),
+    # head_dim 64 over 32-token pages: 64-key chunks spanning two pages on
+    # the shared kernel, with windows and partitions that start mid-chunk
+    ("f16", 4, 64, 32, 0.0, 40, 96, [300, 97, 64], [70, 97, 5]),
+    ("bf16", 8, 64, 32, 30.0, 0, 96, [333, 150, 40], [150, 150, 7]),
 ]
 
 
