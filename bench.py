@@ -415,13 +415,13 @@ def bench_mq(args):
 
 def read_ceiling(pa, torch, dev, gib=4):
     """Best read bandwidth (GB/s) of the library's plain streaming probe
-    (pa_read_bandwidth_probe) over ``gib`` GiB, at three grid sizes: the
+    (pa_read_bandwidth_probe) over ``gib`` GiB, at four grid sizes: the
     practical ceiling next to the data sheet's HBM peak."""
     buf = torch.empty(gib << 28, dtype=torch.float32, device=dev)
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     nbytes = buf.numel() * 4
     best = (0.0, 0)
-    for grid in (4096, 8192, 16384):
+    for grid in (4096, 8192, 16384, 32768):
         for _ in range(2):
             pa.read_bandwidth_probe(buf, grid, sink)
         e0 = torch.cuda.Event(enable_timing=True)
@@ -438,8 +438,9 @@ def read_ceiling(pa, torch, dev, gib=4):
     torch.cuda.empty_cache()
     return {"gbs": round(best[0], 1), "grid": best[1],
             "probe": (f"pa_read_bandwidth_probe: one pass over {gib} GiB, 256-thread workgroups, "
-                      "16-byte non-temporal loads, 8 in flight per thread; best of grids "
-                      "4096/8192/16384, 10 launches each (HIP events)")}
+                      "16-byte non-temporal loads, 8 in flight per thread, one contiguous 32 KB "
+                      "block per workgroup step; best of grids 4096/8192/16384/32768, mean of "
+                      "10 launches each (HIP events)")}
 
 
 def with_ceiling(roof, ceiling):

@@ -188,7 +188,9 @@ int pa_set_decode_events(void* start_event, void* stop_event);
  * Measurement aid, not part of the attention path: one streaming pass that
  * reads `bytes` of device memory at `buf` (16-byte aligned, a multiple of
  * 16 bytes) with `grid` workgroups of 256 threads, 16-byte non-temporal
- * loads, eight in flight per thread.  It gives the read bandwidth a plain
+ * loads, eight in flight per thread, each workgroup step one contiguous
+ * 32 KB block, the blocks dealt to the workgroups in turn.  It gives the
+ * read bandwidth a plain
  * kernel reaches on this GPU: the practical ceiling the memory-bound
  * decode kernels are reported against next to the data sheet's peak.
  * `sink` is a 4-byte device word the kernel may write (it practically never
