@@ -118,7 +118,8 @@ struct Unit {
 // workgroup, or with HEADS by the head's own wavefront).
 template <int DT, int D, int G, bool HEADS = false>
 __device__ __forceinline__ bool unit_range(const DecodeParams& p, Unit& u) {
-  const int L = min(p.context_lens[u.b], p.max_context_len);
+  typedef const __attribute__((address_space(4))) int32_t cint32;
+  const int L = min(((cint32*)p.context_lens)[u.b], p.max_context_len);
   if (L <= 0) {
     const int first = HEADS ? (int)(threadIdx.x & 63) : (int)threadIdx.x;
     const int stride = HEADS ? 64 : (int)blockDim.x;
@@ -250,6 +251,16 @@ __global__ __launch_bounds__(64 * kMaxWaves, PA_DECODE_MIN_WAVES) void decode_ke
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
+  // The parameters a unit's first loads depend on, all read here at once:
+  // left to the compiler, they came in three dependent rounds of kernel
+  // argument loads, each behind a branch, before the sequence's length
+  // could be requested.
+  asm volatile("" ::"s"(p.order), "s"(p.context_lens), "s"(p.block_tables), "s"(p.q),
+               "s"(p.k_cache), "s"(p.v_cache), "s"(p.seq_row), "s"(p.num_seqs),
+               "s"(p.num_kv_heads), "s"(p.max_context_len), "s"(p.max_blocks_per_seq),
+               "s"(p.window), "s"(p.part), "s"(p.xcd_units), "s"(p.log2_bs), "s"(p.num_blocks),
+               "s"(p.num_heads), "s"(p.prio), "s"(p.tail_k), "s"(p.tail_v), "s"(p.tail_slots),
+               "s"(nw));
 
   // per-wavefront LDS, sized by the launch (decode_lds_bytes)
   extern __shared__ __align__(16) float smem[];
