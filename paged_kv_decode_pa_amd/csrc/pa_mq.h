@@ -126,6 +126,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
   // unit: KV head fastest (or the wavefront's head), then tiles (a
   // sequence's tiles side by side, so they share its pages in L2), then
   // partitions
+  // kernel arguments along the unit's lookup chain (tile, sequence start
+  // and length), read in one round, the loads of each link issued together
+  asm volatile("" ::"s"(p.num_kv_heads), "s"(p.num_tiles), "s"(p.tiles), "s"(p.max_tiles),
+               "s"(p.resident_period), "s"(p.resident_span), "s"(p.query_start),
+               "s"(p.context_lens), "s"(p.num_tokens), "s"(p.max_context_len), "s"(p.group),
+               "s"(p.window), "s"(p.part), "s"(p.q), "s"(p.num_heads), "s"(p.block_tables),
+               "s"(p.max_blocks_per_seq), "s"(p.log2_bs), "s"(p.k_cache), "s"(p.v_cache),
+               "s"(p.num_blocks), "s"(nw));
   const int Hq = p.num_heads;
   const int G = p.group;
   const int g = HEADS ? w : (int)(blockIdx.x % p.num_kv_heads);
@@ -140,10 +148,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mq_mfma_kernel(MQParams p) {
   const int b = (int)(uint32_t)tl;
   const int f0 = (int)(uint32_t)(tl >> 32);
   // the sequence's rows, clamped to [0, T) whatever query_start holds
-  const int q0 = min(max(((cint32*)p.query_start)[b], 0), p.num_tokens);
-  const int n = min(max(((cint32*)p.query_start)[b + 1] - q0, 0), p.num_tokens - q0);
+  const int qs_b = ((cint32*)p.query_start)[b];
+  const int qs_b1 = ((cint32*)p.query_start)[b + 1];
+  const int L_raw = ((cint32*)p.context_lens)[b];
+  asm volatile("" ::"s"(qs_b), "s"(qs_b1), "s"(L_raw));  // one round for the three
+  const int q0 = min(max(qs_b, 0), p.num_tokens);
+  const int n = min(max(qs_b1 - q0, 0), p.num_tokens - q0);
   const int f_end = min(f0 + R, n * G);
-  const int L = min(((cint32*)p.context_lens)[b], p.max_context_len);
+  const int L = min(L_raw, p.max_context_len);
   const int W = p.window;
   const int P = p.part;
   auto key_lo = [&](int pos) { return W > 0 ? max(0, pos + 1 - W) : 0; };
@@ -625,27 +637,45 @@ __global__ __launch_bounds__(256, (mq_wg_min_blocks<D, NR, TILES, NBUF_>())) voi
   const int G = p.group;
   // unit: KV head fastest, then the plan's (tile, partition) list, or
   // without one tiles in plan order with partitions slowest
+  // The unit's lookups form a chain (list entry, tile, sequence start and
+  // length); the kernel arguments along it are read in one round here, and
+  // the loads of each link are issued together.  Left to the compiler, the
+  // arguments came in rounds of their own between the links.
+  asm volatile("" ::"s"(p.num_kv_heads), "s"(p.units), "s"(p.num_tiles), "s"(p.tiles),
+               "s"(p.max_tiles), "s"(p.query_start), "s"(p.context_lens), "s"(p.num_tokens),
+               "s"(p.max_context_len), "s"(p.group), "s"(p.window), "s"(p.part), "s"(p.q),
+               "s"(p.num_heads), "s"(p.block_tables), "s"(p.max_blocks_per_seq),
+               "s"(p.log2_bs), "s"(p.k_cache), "s"(p.v_cache), "s"(p.num_blocks));
   const int g = blockIdx.x % p.num_kv_heads;
   const int rest = blockIdx.x / p.num_kv_heads;
   int tile, part;
+  const int n_tiles = *(cint32*)p.num_tiles;
   if (p.units != nullptr) {
-    if (rest >= ((cint32*)p.num_tiles)[1]) return;
+    // the entry is read with the list's length: the list has room for an
+    // entry at every position of the grid, written or not
+    const int n_units = ((cint32*)p.num_tiles)[1];
     const uint64_t u = ((cu64*)p.units)[rest];
+    asm volatile("" ::"s"(n_units), "s"(u), "s"(n_tiles));  // one round for the three
+    if (rest >= n_units) return;
     tile = (int)(uint32_t)u;
     part = (int)(uint32_t)(u >> 32);
-    if (tile >= *(cint32*)p.num_tiles) return;
+    if (tile >= n_tiles) return;
   } else {
     tile = rest % p.max_tiles;
     part = rest / p.max_tiles;
-    if (tile >= *(cint32*)p.num_tiles) return;
+    if (tile >= n_tiles) return;
   }
   const uint64_t tl = ((cu64*)p.tiles)[tile];
   const int b = (int)(uint32_t)tl;
   const int f0 = (int)(uint32_t)(tl >> 32);
-  const int q0 = min(max(((cint32*)p.query_start)[b], 0), p.num_tokens);
-  const int n = min(max(((cint32*)p.query_start)[b + 1] - q0, 0), p.num_tokens - q0);
+  const int qs_b = ((cint32*)p.query_start)[b];
+  const int qs_b1 = ((cint32*)p.query_start)[b + 1];
+  const int L_raw = ((cint32*)p.context_lens)[b];
+  asm volatile("" ::"s"(qs_b), "s"(qs_b1), "s"(L_raw));  // one round for the three
+  const int q0 = min(max(qs_b, 0), p.num_tokens);
+  const int n = min(max(qs_b1 - q0, 0), p.num_tokens - q0);
   const int f_end = min(f0 + R, n * G);
-  const int L = min(((cint32*)p.context_lens)[b], p.max_context_len);
+  const int L = min(L_raw, p.max_context_len);
   const int W = p.window;
   const int P = p.part;
   auto key_lo = [&](int pos) { return W > 0 ? max(0, pos + 1 - W) : 0; };
